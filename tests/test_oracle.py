@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests re-types the oracle's own formula: each compares it with
+an independent source -- NumPy's / torch's IEEE conversions, SciPy's Hadamard
+construction, hand-derived fixtures in tests/golden/, closed forms,
+invariants, or a brute-force Python loop on tiny inputs.  Citations name the
+page and section each check follows.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from gemm_kq_gemv_amd import inputs
+from tests import _golden as G
+
+pytestmark = pytest.mark.usefixtures("oracle_lib")
+
+
+# --------------------------------------------------------------------------
+# fp16 / bf16 codecs (IEEE 754; checked against NumPy and torch)
+# --------------------------------------------------------------------------
+
+def test_f16_decode_exhaustive_vs_numpy():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f32_from_f16(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_roundtrip_exhaustive():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.f32_from_f16(h)
+    keep = ~np.isnan(f)
+    assert np.array_equal(oracle.f16_from_f32(f[keep]), h[keep])
+
+
+def test_f16_encode_ties_and_random_vs_numpy():
+    # every midpoint between consecutive finite halves (exact in fp32), the
+    # midpoints' neighbours, and a wide random sample
+    h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    hi[-1] = 65536.0  # the next binade's first value past 65504
+    mid = ((lo + hi) / 2).astype(np.float32)
+    cases = [mid, np.nextafter(mid, np.float32(np.inf)),
+             np.nextafter(mid, np.float32(0))]
+    r = inputs.rng(7)
+    cases.append((r.standard_normal(200000) *
+                  np.exp2(r.integers(-30, 17, 200000))).astype(np.float32))
+    cases.append(np.array([0.0, 65504.0, 65519.996, 65520.0, 1e30, 2.0 ** -25,
+                           2.0 ** -24, 3 * 2.0 ** -26, 2.0 ** -126, 1e-40],
+                          dtype=np.float32))
+    a = np.concatenate(cases)
+    a = np.concatenate([a, -a])
+    with np.errstate(over="ignore"):
+        ref = a.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f16_from_f32(a), ref)
+
+
+def test_bf16_vs_torch():
+    import torch
+    b = np.arange(0, 0x7F80, dtype=np.uint32)
+    lo = (b << 16).view(np.float32).astype(np.float64)
+    hi = ((b + 1) << 16).view(np.float32).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)  # exact: needs 9 significant bits
+    r = inputs.rng(8)
+    rnd = (r.standard_normal(100000) * np.exp2(r.integers(-120, 120, 100000))).astype(np.float32)
+    a = np.concatenate([mid, np.nextafter(mid, np.float32(np.inf)), rnd,
+                        np.array([3.3895e38, 3.4e38, np.inf], dtype=np.float32)])
+    a = np.concatenate([a, -a])
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_from_f32(a), ref)
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    wide = oracle.f32_from_bf16(allb)
+    tref = torch.from_numpy(allb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(tref)
+    assert np.array_equal(np.isnan(wide), nan)
+    assert np.array_equal(wide[~nan].view(np.uint32), tref[~nan].view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# PQ2_0 format: decode table, positions, word view (Bonsai page sec. 3.1)
+# --------------------------------------------------------------------------
+
+def _aos_block(d16: int, qs: np.ndarray) -> np.ndarray:
+    return np.concatenate([np.array([d16 & 0xFF, d16 >> 8], dtype=np.uint8), qs])
+
+
+def test_pq2_decode_fixture():
+    g = G.load("pq2_decode_block.txt")
+    blk = _aos_block(int(g["d16"], 16), G.hex_bytes(g["qs"]))
+    assert blk.size == 34
+    want = np.zeros(128)
+    want[:32] = G.floats(g["values"])
+    assert np.array_equal(oracle.unpack_pq2_aos(blk, 1, 128)[0], want)
+    assert np.array_equal(oracle.unpack_pq2_aos(blk, 1, 128, word_view=True)[0], want)
+
+
+def test_pq2_byte_view_equals_word_view_random_blobs():
+    N, K = 7, 384
+    blob = inputs.random_bytes(11, N * (K // 128) * 34)
+    # keep the scales finite so values compare with ==
+    for b in range(N * K // 128):
+        blob[b * 34 + 1] &= 0x3F
+    a = oracle.unpack_pq2_aos(blob, N, K)
+    b = oracle.unpack_pq2_aos(blob, N, K, word_view=True)
+    assert np.array_equal(a, b)
+
+
+def test_pq2_quantize_fixture():
+    g = G.load("pq2_quantize_blocks.txt")
+    W = np.stack([G.sparse_block(g[f"block{c}_w"], 128) for c in "ABCD"])
+    aos = oracle.pack_pq2_aos(W).reshape(4, 34)
+    for i, c in enumerate("ABCD"):
+        d16 = int(g[f"block{c}_d16"], 16)
+        assert int(aos[i, 0]) | (int(aos[i, 1]) << 8) == d16, c
+        assert np.array_equal(aos[i, 2:], G.hex_bytes(g[f"block{c}_qs"])), c
+
+
+def test_pq2_quantizer_invariants_gaussian():
+    N, K = 64, 1024
+    W = inputs.weights(3, N, K)
+    aos = oracle.pack_pq2_aos(W)
+    blocks = aos.reshape(N * K // 128, 34)
+    qs = blocks[:, 2:]
+    codes = np.stack([(qs >> (2 * s)) & 3 for s in range(4)], axis=-1).reshape(-1, 128).astype(np.int64)
+    assert not np.any(codes == 3)                     # "code 3 never occurs"
+    d16 = blocks[:, 0].astype(np.uint16) | (blocks[:, 1].astype(np.uint16) << 8)
+    dF = d16.view(np.float16).astype(np.float64)      # numpy decode of d
+    Wb = W.reshape(-1, 128).astype(np.float64)
+    amax = np.abs(Wb).max(axis=1)
+    assert np.array_equal(dF, amax.astype(np.float16).astype(np.float64))
+    deq = (codes - 1) * dF[:, None]
+    # the arg-max element decodes to +-d exactly
+    am = np.abs(Wb).argmax(axis=1)
+    rows = np.arange(Wb.shape[0])
+    assert np.array_equal(np.abs(deq[rows, am]), dF)
+    assert np.array_equal(np.sign(deq[rows, am]), np.sign(Wb[rows, am]))
+    # nearest ternary level: |w - deq| <= d/2 (tiny slack for the fp32 division)
+    assert np.all(np.abs(Wb - deq) <= 0.5 * dF[:, None] * (1 + 2 ** -20))
+    # oracle decode agrees with this numpy reading
+    assert np.array_equal(oracle.unpack_pq2_aos(aos, N, K).reshape(-1, 128), deq)
+    # idempotent: quantizing the decoded weights reproduces the bytes
+    again = oracle.pack_pq2_aos(deq.reshape(N, K).astype(np.float32))
+    assert np.array_equal(again, aos)
+    # histogram of a Gaussian block at d = max|w|: ~8%/84%/8% (sanity only)
+    frac = np.bincount(codes.reshape(-1), minlength=3) / codes.size
+    assert 0.05 < frac[0] < 0.12 and 0.76 < frac[1] < 0.9 and 0.05 < frac[2] < 0.12
+
+
+def test_pq2_aos_to_planar_layout():
+    N, K = 3, 256
+    W = inputs.weights(4, N, K)
+    aos = oracle.pack_pq2_aos(W).reshape(N, K // 128, 34)
+    pl = oracle.aos_to_planar(oracle.FMT_PQ2_0, aos, N, K)
+    qs_bytes = N * K // 4
+    d_off = (qs_bytes + 255) // 256 * 256
+    assert pl.size == d_off + N * (K // 128) * 2
+    assert np.array_equal(pl[:qs_bytes].reshape(N, K // 128, 32), aos[:, :, 2:])
+    assert np.array_equal(pl[d_off:].reshape(N, K // 128, 2), aos[:, :, :2])
+    # word view of the plane: element 16i + j of a row at bits 2j of LE word i
+    words = pl[:qs_bytes].view("<u4").reshape(N, K // 16)
+    codes = np.stack([(words >> (2 * j)) & 3 for j in range(16)], axis=-1).reshape(N, K)
+    dF = pl[d_off:].view("<f2").astype(np.float64).reshape(N, K // 128)
+    deq = (codes.astype(np.float64) - 1) * np.repeat(dF, 128, axis=1)
+    assert np.array_equal(deq, oracle.unpack_pq2_aos(aos.reshape(-1), N, K))
+
+
+# --------------------------------------------------------------------------
+# Q8_0 format
+# --------------------------------------------------------------------------
+
+def test_q8_quantize_fixture():
+    g = G.load("q8_quantize_block.txt")
+    W = G.sparse_block(g["w"], 32)[None, :]
+    aos = oracle.pack_q8_aos(W)
+    assert int(aos[0]) | (int(aos[1]) << 8) == int(g["d16"], 16)
+    assert np.array_equal(aos[2:].view(np.int8).astype(np.int64), G.ints(g["q"]))
+    deq = oracle.unpack_q8_aos(aos, 1, 32)[0]
+    assert np.array_equal(deq, G.ints(g["q"]).astype(np.float64) * 1.0)
+    W2 = G.sparse_block(g["b2_w"], 32)[None, :]
+    aos2 = oracle.pack_q8_aos(W2)
+    assert int(aos2[0]) | (int(aos2[1]) << 8) == int(g["b2_d16"], 16)
+    assert np.array_equal(aos2[2:].view(np.int8).astype(np.int64), G.ints(g["b2_q"]))
+
+
+def test_q8_quantizer_invariants_gaussian():
+    N, K = 48, 512
+    W = inputs.weights(5, N, K)
+    aos = oracle.pack_q8_aos(W)
+    blocks = aos.reshape(-1, 34)
+    q = blocks[:, 2:].view(np.int8).astype(np.int64)
+    dF = blocks[:, :2].copy().view("<f2").astype(np.float64)[:, 0]
+    Wb = W.reshape(-1, 32).astype(np.float64)
+    amax = np.abs(Wb).max(axis=1)
+    d32 = (amax.astype(np.float32) / np.float32(127)).astype(np.float32)
+    assert np.array_equal(dF, d32.astype(np.float16).astype(np.float64))
+    am = np.abs(Wb).argmax(axis=1)
+    assert np.array_equal(np.abs(q[np.arange(len(am)), am]), np.full(len(am), 127))
+    deq = q * dF[:, None]
+    assert np.all(np.abs(Wb - deq) <= 0.5 * dF[:, None] * (1 + 2 ** -20))
+    assert np.array_equal(oracle.unpack_q8_aos(aos, N, K).reshape(-1, 32), deq)
+    assert np.array_equal(oracle.pack_q8_aos(deq.reshape(N, K).astype(np.float32)), aos)
+
+
+def test_q8_zero_block_and_planar():
+    N, K = 2, 64
+    W = np.zeros((N, K), dtype=np.float32)
+    W[1, 40] = -3.0
+    aos = oracle.pack_q8_aos(W).reshape(N, 2, 34)
+    assert np.all(aos[0] == 0)                 # d = 0, q = 0
+    assert np.all(aos[1, 0] == 0)
+    pl = oracle.aos_to_planar(oracle.FMT_Q8_0, aos, N, K)
+    d_off = 256
+    assert np.array_equal(pl[:N * K].reshape(N, 2, 32), aos[:, :, 2:])
+    assert np.array_equal(pl[d_off:].reshape(N, 2, 2), aos[:, :, :2])
+    assert pl[N * K:d_off].sum() == 0
+
+
+# --------------------------------------------------------------------------
+# Rotation (Bonsai page sec. 4.1, 4.2)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024])
+def test_hadamard_matches_scipy_sylvester(n):
+    H = oracle.hadamard_matrix(n).astype(np.int64)
+    assert np.array_equal(H, scipy.linalg.hadamard(n))
+    assert np.array_equal(H @ H.T, n * np.eye(n, dtype=np.int64))
+    assert np.array_equal(H, H.T)
+    if n >= 2:
+        h = oracle.hadamard_matrix(n // 2).astype(np.int64)
+        assert np.array_equal(H, np.block([[h, h], [h, -h]]))
+
+
+def test_hadamard_golden_examples():
+    g = G.load("hadamard_examples.txt")
+    H4 = np.stack([G.ints(g[f"H4_row{r}"]) for r in range(4)])
+    assert np.array_equal(oracle.hadamard_matrix(4), H4)
+    for ex in ("ex1", "ex2", "ex3"):
+        x = G.floats(g[f"{ex}_x"])
+        s = G.ints(g[f"{ex}_signs"]).astype(np.int8)
+        want = G.floats(g[f"{ex}_xr"])
+        got = oracle.rotate(x, len(x), s)
+        assert np.allclose(got, want, rtol=0, atol=1e-15), ex
+
+
+def _fwht_py(v):
+    """Textbook in-place fast Walsh-Hadamard butterflies (natural order)."""
+    v = list(v)
+    h = 1
+    while h < len(v):
+        for i in range(0, len(v), 2 * h):
+            for j in range(i, i + h):
+                a, b = v[j], v[j + h]
+                v[j], v[j + h] = a + b, a - b
+        h *= 2
+    return v
+
+
+@pytest.mark.parametrize("n", [2, 16, 128])
+def test_rotation_properties(n):
+    K = 4 * n
+    x = inputs.gaussian(21, (3, K)).astype(np.float64)
+    s = inputs.signs(22, K)
+    xr = oracle.rotate(x, n, s)
+    # butterflies (independent construction) == explicit matrix
+    for m in range(3):
+        sx = np.where(s < 0, -x[m], x[m])
+        for b in range(K // n):
+            want = np.array(_fwht_py(sx[b * n:(b + 1) * n])) / math.sqrt(n)
+            assert np.allclose(xr[m, b * n:(b + 1) * n], want, rtol=0, atol=1e-12)
+    # orthogonality: Parseval, and R^T R = I (R twice = I without signs)
+    assert np.allclose(np.linalg.norm(xr, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    assert np.allclose(oracle.rotate(oracle.rotate(x, n), n), x, rtol=0, atol=1e-12)
+    # block-diagonal with SciPy's Sylvester matrix
+    Hs = scipy.linalg.block_diag(*([scipy.linalg.hadamard(n)] * (K // n))) / math.sqrt(n)
+    assert np.allclose(xr, (Hs @ (x * s).T).T, rtol=0, atol=1e-12)
+
+
+def test_rotation_one_hot_pins_sign_then_transform():
+    n, K = 8, 16
+    s = inputs.signs(5, K)
+    H = scipy.linalg.hadamard(n)
+    for k in range(K):
+        e = np.zeros(K)
+        e[k] = 1.0
+        got = oracle.rotate(e, n, s)
+        b, c = divmod(k, n)
+        want = np.zeros(K)
+        want[b * n:(b + 1) * n] = s[k] * H[:, c] / math.sqrt(n)
+        assert np.allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_rotation_block_len_zero_is_sign_only():
+    x = inputs.gaussian(1, (2, 64)).astype(np.float64)
+    s = inputs.signs(2, 64)
+    assert np.array_equal(oracle.rotate(x, 0, s), x * s)
+    assert np.array_equal(oracle.rotate(x, 0), x)
+
+
+# --------------------------------------------------------------------------
+# Product: brute force, closed forms, fold invariant
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,M,n", [(1, 128, 1, 128), (5, 256, 2, 128),
+                                     (8, 128, 3, 32), (3, 256, 1, 0)])
+def test_pq2_product_brute_force(N, K, M, n):
+    W = inputs.weights(31, N, K)
+    x = inputs.activations(32, M, K, offset=0.25)
+    s = inputs.signs(33, K)
+    aos = oracle.pack_pq2_aos(W)
+    y, bnd = oracle.gemv_aos(oracle.FMT_PQ2_0, aos, N, K, x, n, s)
+    xr = oracle.rotate(x.astype(np.float64), n, s)
+    blocks = aos.reshape(N, K // 128, 34)
+    for m in range(M):
+        for r in range(N):
+            # code-sum form: y = sum_b d_b (sum_{q=2} x' - sum_{q=0} x')
+            tot, tot_abs = 0.0, 0.0
+            for b in range(K // 128):
+                blk = blocks[r, b]
+                d = float(np.frombuffer(blk[:2].tobytes(), dtype="<f2")[0])
+                plus = minus = 0.0
+                for j in range(128):
+                    q = (int(blk[2 + j // 4]) >> (2 * (j % 4))) & 3
+                    v = xr[m, b * 128 + j]
+                    if q == 2:
+                        plus += v
+                    elif q == 0:
+                        minus += v
+                    tot_abs += abs(v) * d * abs(q - 1)
+                tot += d * (plus - minus)
+            assert abs(y[m, r] - tot) <= 1e-12 * max(1.0, tot_abs)
+            assert abs(bnd[m, r] - tot_abs) <= 1e-12 * max(1.0, tot_abs)
+
+
+@pytest.mark.parametrize("N,K,M", [(3, 64, 1), (2, 96, 2)])
+def test_q8_product_brute_force(N, K, M):
+    W = inputs.weights(41, N, K)
+    x = inputs.activations(42, M, K, offset=-0.5)
+    aos = oracle.pack_q8_aos(W)
+    y, bnd = oracle.gemv_aos(oracle.FMT_Q8_0, aos, N, K, x, 0)
+    blocks = aos.reshape(N, K // 32, 34)
+    for m in range(M):
+        for r in range(N):
+            tot = 0.0
+            for b in range(K // 32):
+                d = float(np.frombuffer(blocks[r, b, :2].tobytes(), dtype="<f2")[0])
+                for j in range(32):
+                    q = int(np.int8(blocks[r, b, 2 + j]))
+                    tot += d * q * float(x[m, b * 32 + j])
+            assert abs(y[m, r] - tot) <= 1e-12 * max(1.0, bnd[m, r])
+
+
+def test_all_plus_one_row_closed_form():
+    # every code 2 with d = 1, no signs: column sums of Sylvester H are
+    # n * delta_{c0}, so y = sum_b sqrt(n) * x[b*n]
+    n, K = 128, 512
+    W = np.ones((1, K), dtype=np.float32)
+    x = inputs.activations(51, 1, K)
+    y, _ = oracle.gemv_aos(oracle.FMT_PQ2_0, oracle.pack_pq2_aos(W), 1, K, x, n)
+    want = math.sqrt(n) * sum(float(x[0, b * n]) for b in range(K // n))
+    assert abs(y[0, 0] - want) <= 1e-12 * abs(want) + 1e-12
+
+
+def test_one_hot_row_picks_rotated_element():
+    n, K = 128, 256
+    x = inputs.activations(52, 1, K)
+    s = inputs.signs(53, K)
+    xr = oracle.rotate(x.astype(np.float64), n, s)
+    for k in (0, 1, 127, 128, 200):
+        W = np.zeros((1, K), dtype=np.float32)
+        W[0, k] = 0.75                              # d = 0.75, code 2 at k
+        y, _ = oracle.gemv_aos(oracle.FMT_PQ2_0, oracle.pack_pq2_aos(W), 1, K, x, n, s)
+        assert abs(y[0, 0] - 0.75 * xr[0, k]) <= 1e-14
+
+
+def test_fold_invariant():
+    # Bonsai page sec. 4.2: stored W' = W R^T, runtime y = W' (R x) = W x
+    n, K, N = 128, 384, 6
+    W = inputs.weights(61, N, K).astype(np.float64)
+    x = inputs.activations(62, 1, K).astype(np.float64)
+    s = inputs.signs(63, K)
+    Wf = oracle.rotate(W, n, s)            # each row w -> R w, i.e. W R^T
+    xr = oracle.rotate(x, n, s)
+    y, _ = oracle.matmul(Wf, xr)
+    assert np.allclose(y[0], W @ x[0], rtol=1e-12, atol=1e-12)
+
+
+def test_matmul_vs_numpy_and_bound():
+    N, K, M = 7, 200, 3
+    W = inputs.gaussian(71, (N, K)).astype(np.float64)
+    xr = inputs.gaussian(72, (M, K)).astype(np.float64)
+    y, b = oracle.matmul(W, xr)
+    assert np.allclose(y, xr @ W.T, rtol=1e-13, atol=1e-13)
+    assert np.allclose(b, np.abs(xr) @ np.abs(W).T, rtol=1e-13)
+    assert np.all(b >= np.abs(y))
+
+
+def test_bad_shapes_rejected():
+    with pytest.raises(ValueError):
+        oracle.pack_pq2_aos(np.zeros((1, 100), np.float32))
+    with pytest.raises(ValueError):
+        oracle.rotate(np.zeros(96), 64)
+    with pytest.raises(ValueError):
+        oracle.hadamard_matrix(12)
