@@ -1,0 +1,275 @@
+"""Benchmark of the quantized GEMV hot path on one MI355X.
+
+Headline workload: PQ2_0 GEMV, K=5120, N=10240, M=1 (the fused-QKV shape of
+the Bonsai 27B decoder), activation rotated by a blockwise Walsh-Hadamard
+transform with block 128.  One step = one kq_gemv call (rotation pre-pass +
+GEMV) over one activation vector; inputs are resident in HBM.  40 distinct
+packed weight copies (557 MB > 2 x 256 MB MALL) are used in turn so that every
+step streams its weights from HBM rather than from the Infinity Cache.  The
+timed loop replays a captured HIP graph of 40 steps (launch-bound inner loop);
+eager-launch timing is reported beside it.
+
+Prints ONE JSON line.  `value` = streamed weight bytes per step / step time.
+`roofline` is for the dominant kernel (the GEMV itself, timed alone with HIP
+events on its stream); `cpu_baseline` times the C oracle on the host cores.
+"""
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+N_COPIES = 40
+
+
+def gbs(nbytes, seconds):
+    return nbytes / seconds / 1e9
+
+
+def time_graph(fn_list, replays, warmup, stream):
+    """Capture fn_list (closures that enqueue work) as one graph, replay it
+    `replays` times; returns seconds per replay (HIP events on `stream`)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for f in fn_list:        # warm the code paths before capture
+            f()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fn_list:
+            f()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / replays, g
+
+
+def time_eager(fn_list, reps, stream):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for f in fn_list:
+            f()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            for f in fn_list:
+                f()
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (reps * len(fn_list))
+
+
+def cpu_baseline(W, x, N, K, n, budget_s=10.0):
+    """The oracle as it stands (unpack, explicit-matrix rotation, binary64
+    product), on the host cores, over whole C2 calls until ~budget_s."""
+    import oracle
+    aos = oracle.pack_pq2_aos(W)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemv_aos(oracle.FMT_PQ2_0, aos, N, K, x, n)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_call = el / calls
+    return {"value": round(gbs(N * K // 128 * 34, per_call), 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{calls} full K=5120 N=10240 M=1 calls (unpack + rotate + fp64 product), "
+                      f"{per_call * 1e3:.1f} ms per call"}
+
+
+def extras(kq, inputs, stream, quick):
+    """Throughput of the other configurations (reported, not the headline)."""
+    import numpy as np
+    import torch
+    out = {}
+    # Q8_0 GEMV K=5120 N=17408, M in {1,4,8}
+    N, K = 17408, 5120
+    W = torch.from_numpy(inputs.weights(1004, N, K)).cuda()
+    p8 = kq.pack(kq.KQ_FMT_Q8_0, W)
+    del W
+    copies = [p8] + [p8.clone() for _ in range(5)]
+    wbytes = N * K // 32 * 34
+    for M in (1, 4, 8):
+        x = torch.from_numpy(inputs.activations(2004, M, K)).cuda()
+        ws, nws = kq.workspace(0, kq.KQ_FMT_Q8_0, M, N, K, 0)
+        y = torch.empty((M, N), device="cuda")
+        fns = [(lambda c=c: kq.kq_gemv(kq.KQ_FMT_Q8_0, c, N, K, x, M, 0, None, 0, y, ws, nws))
+               for c in copies]
+        t, _ = time_graph(fns, 20, 3, stream)
+        t /= len(fns)
+        out[f"q8_gemv_k5120_n17408_m{M}"] = {
+            "us_per_call": round(t * 1e6, 3), "weight_GBs": round(gbs(wbytes, t), 1),
+            "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4)}
+    del copies, p8
+    # PQ2_0 lm_head GEMV K=5120 N=248320 (split-K 1, 2, 4)
+    N = 248320
+    W = torch.from_numpy(inputs.weights(1003, N, K)).cuda()
+    ph = kq.pack(kq.KQ_FMT_PQ2_0, W)
+    del W
+    torch.cuda.empty_cache()
+    heads = [ph, ph.clone()]
+    x = torch.from_numpy(inputs.activations(2003, 1, K)).cuda()
+    wbytes = N * K // 128 * 34
+    for S in (1, 2, 4):
+        ws, nws = kq.workspace(0, kq.KQ_FMT_PQ2_0, 1, N, K, 128, S)
+        y = torch.empty((1, N), device="cuda")
+        fns = [(lambda c=c: kq.kq_gemv(kq.KQ_FMT_PQ2_0, c, N, K, x, 1, 128, None, S, y, ws, nws))
+               for c in heads]
+        t, _ = time_graph(fns, 10, 2, stream)
+        t /= len(fns)
+        out[f"pq2_gemv_k5120_n248320_split{S}"] = {
+            "us_per_call": round(t * 1e6, 2), "weight_GBs": round(gbs(wbytes, t), 1),
+            "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4)}
+    del heads, ph
+    torch.cuda.empty_cache()
+    # PQ2_0 prefill GEMM M=2048 K=5120 N=10240 (bf16 MFMA)
+    M, N = 2048, 10240
+    W = torch.from_numpy(inputs.weights(1005, N, K)).cuda()
+    pg = kq.pack(kq.KQ_FMT_PQ2_0, W)
+    del W
+    xb = torch.from_numpy(inputs.to_bf16_bits(inputs.activations(2005, M, K)).view(np.int16)).cuda().view(torch.bfloat16)
+    ws, nws = kq.workspace(1, kq.KQ_FMT_PQ2_0, M, N, K, 128)
+    y = torch.empty((M, N), device="cuda")
+    fns = [lambda: kq.kq_gemm(kq.KQ_FMT_PQ2_0, pg, N, K, xb, kq.KQ_BF16, M, 128, None, y, ws, nws)]
+    t, _ = time_graph(fns, 20, 3, stream)
+    flops = 2.0 * M * N * K
+    out["pq2_gemm_m2048_k5120_n10240"] = {
+        "us_per_call": round(t * 1e6, 2), "TFLOPs": round(flops / t / 1e12, 1),
+        "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    # Hadamard pre-pass of the GEMM input, bf16 -> bf16
+    xr = torch.empty_like(xb)
+    fns = [lambda: kq.kq_hadamard_blocks(xb, kq.KQ_BF16, xr, kq.KQ_BF16, M, K, 128, None)]
+    t, _ = time_graph(fns, 50, 3, stream)
+    out["hadamard_bf16_m2048_k5120"] = {"us_per_call": round(t * 1e6, 2),
+                                        "GBs": round(gbs(2 * 2 * M * K, t), 1)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the single-GPU kernel is the measured unit; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_kq_gemv_amd as kq
+    from gemm_kq_gemv_amd import inputs
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    N, K, M, n = 10240, 5120, 1, 128
+    W_host = inputs.weights(1002, N, K)
+    x_host = inputs.activations(2002, M, K)
+    packed0 = kq.pack(kq.KQ_FMT_PQ2_0, torch.from_numpy(W_host).cuda())
+    copies = [packed0] + [packed0.clone() for _ in range(N_COPIES - 1)]
+    x = torch.from_numpy(x_host).cuda()
+    ws, nws = kq.workspace(0, kq.KQ_FMT_PQ2_0, M, N, K, n)
+    y = torch.empty((M, N), device="cuda")
+    weight_bytes = N * K // 128 * 34
+    algo_bytes = weight_bytes + M * K * 4 + M * N * 4
+
+    def step(c):
+        return lambda: kq.kq_gemv(kq.KQ_FMT_PQ2_0, c, N, K, x, M, n, None, 1, y, ws, nws)
+
+    steps = [step(c) for c in copies]
+    replays = max(1, args.steps // len(steps))
+    warm = max(1, args.warmup // len(steps))
+    n_steps = replays * len(steps)
+    torch.cuda.synchronize()
+    t_rep, graph = time_graph(steps, replays, warm, stream)
+    t_step = t_rep / len(steps)
+    t_step_eager = time_eager(steps, max(1, replays // 4), stream)
+
+    # the dominant kernel alone: GEMV on a pre-rotated x' (block_len 0 -> one launch)
+    xr = kq.hadamard(x, n)
+    gemv_only = [(lambda c=c: kq.kq_gemv(kq.KQ_FMT_PQ2_0, c, N, K, xr, M, 0, None, 1, y, ws, nws))
+                 for c in copies]
+    t_k, _ = time_graph(gemv_only, replays, warm, stream)
+    t_kernel = t_k / len(gemv_only)
+    had_only = [lambda: kq.kq_hadamard_blocks(x, kq.KQ_F32, xr, kq.KQ_F32, M, K, n, None)]
+    t_h, _ = time_graph(had_only * len(steps), max(1, replays // 4), 2, stream)
+    t_had = t_h / len(steps)
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "gemv_pq2_k5120_n10240_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tj = json.load(f)
+        if tj.get("kernel_source_sha") == kernel_source_sha():
+            traffic = tj.get("bytes_per_launch")
+
+    value = gbs(weight_bytes, t_step)
+    result = {
+        "metric": "streamed weight GB/s and % of HBM peak, PQ2_0 GEMV K=5120 N=10240 batch 1",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": warm * len(steps),
+        "ms_per_step": round(t_step * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "PQ2_0 GEMV y = W (H_128 x), K=5120, N=10240, M=1, fp32 x/y; "
+                               "40 rotating packed weight copies; graph-replayed steps",
+                   "K": K, "N": N, "M": M, "block_len": n, "weight_bytes": weight_bytes},
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "gemv_calls_per_s": round(1.0 / t_step, 1),
+        "us_per_step_eager": round(t_step_eager * 1e6, 3),
+        "us_gemv_kernel": round(t_kernel * 1e6, 3),
+        "us_hadamard_prepass": round(t_had * 1e6, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs(algo_bytes, t_kernel), 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs(algo_bytes, t_kernel) / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_extras:
+        try:
+            result["others"] = extras(kq, inputs, stream, False)
+        except Exception as e:  # the headline line must still print
+            result["others"] = {"error": repr(e)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(W_host, x_host, N, K, n, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "kq_device.h"):
+        with open(os.path.join(ROOT, "gemm_kq_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

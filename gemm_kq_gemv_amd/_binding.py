@@ -1,0 +1,202 @@
+"""ctypes binding for libkq.so -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls (see
+include/kq.h) and does nothing but turn tensors into device pointers, pick
+the current HIP stream and turn a non-zero kq_status into a KQError.  All
+arithmetic happens in the HIP kernels behind the C ABI; there is no fallback:
+if libkq.so is missing, importing this module raises.
+
+Pointer arguments accept a torch tensor (its data_ptr), None (NULL) or a raw
+integer address.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m gemm_kq_gemv_amd.build or __graft_entry__.build())")
+
+_lib = C.CDLL(LIB_PATH)
+
+KQ_FMT_PQ2_0 = 1
+KQ_FMT_Q8_0 = 2
+KQ_F32 = 0
+KQ_BF16 = 1
+KQ_OK = 0
+STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_EALIGN",
+                4: "KQ_EWORKSPACE", 5: "KQ_EUNSUPPORTED", 6: "KQ_EDEVICE"}
+
+# exported symbols, in include/kq.h order
+EXPORTS = ("kq_status_string", "kq_packed_bytes", "kq_pack_pq2", "kq_pack_q8",
+           "kq_unpack", "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv",
+           "kq_gemm")
+
+_p = C.c_void_p
+_i64 = C.c_int64
+_i32 = C.c_int32
+_lib.kq_status_string.restype = C.c_char_p
+_lib.kq_status_string.argtypes = [C.c_int]
+_lib.kq_packed_bytes.restype = C.c_size_t
+_lib.kq_packed_bytes.argtypes = [C.c_int, _i64, _i64]
+for _n in ("kq_pack_pq2", "kq_pack_q8"):
+    getattr(_lib, _n).restype = C.c_int
+    getattr(_lib, _n).argtypes = [_p, _i64, _i64, _p, _p]
+_lib.kq_unpack.restype = C.c_int
+_lib.kq_unpack.argtypes = [C.c_int, _p, _i64, _i64, _p, _p]
+_lib.kq_hadamard_blocks.restype = C.c_int
+_lib.kq_hadamard_blocks.argtypes = [_p, C.c_int, _p, C.c_int, _i64, _i64, _i32, _p, _p]
+_lib.kq_workspace_bytes.restype = C.c_size_t
+_lib.kq_workspace_bytes.argtypes = [_i32, C.c_int, _i64, _i64, _i64, _i32, _i32]
+_lib.kq_gemv.restype = C.c_int
+_lib.kq_gemv.argtypes = [C.c_int, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p,
+                         C.c_size_t, _p]
+_lib.kq_gemm.restype = C.c_int
+_lib.kq_gemm.argtypes = [C.c_int, _p, _i64, _i64, _p, C.c_int, _i64, _i32, _p, _p, _p,
+                         C.c_size_t, _p]
+
+
+class KQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{where}: {kq_status_string(status)}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != KQ_OK:
+        raise KQError(rc, where)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return KQ_F32
+    if t.dtype == torch.bfloat16:
+        return KQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def kq_status_string(status: int) -> str:
+    return _lib.kq_status_string(status).decode()
+
+
+def kq_packed_bytes(fmt: int, N: int, K: int) -> int:
+    return int(_lib.kq_packed_bytes(fmt, N, K))
+
+
+def kq_pack_pq2(W, N: int, K: int, packed, stream=None):
+    _check(_lib.kq_pack_pq2(_ptr(W), N, K, _ptr(packed), _stream(stream)), "kq_pack_pq2")
+
+
+def kq_pack_q8(W, N: int, K: int, packed, stream=None):
+    _check(_lib.kq_pack_q8(_ptr(W), N, K, _ptr(packed), _stream(stream)), "kq_pack_q8")
+
+
+def kq_unpack(fmt: int, packed, N: int, K: int, W_out, stream=None):
+    _check(_lib.kq_unpack(fmt, _ptr(packed), N, K, _ptr(W_out), _stream(stream)), "kq_unpack")
+
+
+def kq_hadamard_blocks(x, x_dt: int, xr, xr_dt: int, M: int, K: int, block_len: int,
+                       signs=None, stream=None):
+    _check(_lib.kq_hadamard_blocks(_ptr(x), x_dt, _ptr(xr), xr_dt, M, K, block_len,
+                                   _ptr(signs), _stream(stream)), "kq_hadamard_blocks")
+
+
+def kq_workspace_bytes(op: int, fmt: int, M: int, N: int, K: int, block_len: int,
+                       split_k: int = 0) -> int:
+    return int(_lib.kq_workspace_bytes(op, fmt, M, N, K, block_len, split_k))
+
+
+def kq_gemv(fmt: int, packed, N: int, K: int, x, M: int, block_len: int, signs,
+            split_k: int, y, workspace, ws_bytes: int, stream=None):
+    _check(_lib.kq_gemv(fmt, _ptr(packed), N, K, _ptr(x), M, block_len, _ptr(signs),
+                        split_k, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)),
+           "kq_gemv")
+
+
+def kq_gemm(fmt: int, packed, N: int, K: int, x, x_dt: int, M: int, block_len: int,
+            signs, y, workspace, ws_bytes: int, stream=None):
+    _check(_lib.kq_gemm(fmt, _ptr(packed), N, K, _ptr(x), x_dt, M, block_len, _ptr(signs),
+                        _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)), "kq_gemm")
+
+
+# ---- allocation conveniences (torch.empty + one call above) -----------------
+
+def pack(fmt: int, W, stream=None):
+    """Pack fp32 device weights W [N][K]; returns the planar uint8 buffer."""
+    import torch
+    N, K = W.shape
+    out = torch.empty(kq_packed_bytes(fmt, N, K), dtype=torch.uint8, device=W.device)
+    (kq_pack_pq2 if fmt == KQ_FMT_PQ2_0 else kq_pack_q8)(W, N, K, out, stream)
+    return out
+
+
+def unpack(fmt: int, packed, N: int, K: int, stream=None):
+    import torch
+    out = torch.empty((N, K), dtype=torch.float32, device=packed.device)
+    kq_unpack(fmt, packed, N, K, out, stream)
+    return out
+
+
+def hadamard(x, block_len: int, signs=None, out_dtype=None, stream=None):
+    import torch
+    M, K = x.shape
+    out = torch.empty((M, K), dtype=out_dtype or x.dtype, device=x.device)
+    kq_hadamard_blocks(x, _dtype_code(x), out, _dtype_code(out), M, K, block_len, signs, stream)
+    return out
+
+
+def workspace(op: int, fmt: int, M: int, N: int, K: int, block_len: int, split_k: int = 0,
+              device="cuda"):
+    import torch
+    n = kq_workspace_bytes(op, fmt, M, N, K, block_len, split_k)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def gemv(fmt: int, packed, N: int, K: int, x, block_len: int, signs=None, split_k: int = 0,
+         ws=None, y=None, stream=None):
+    import torch
+    M = x.shape[0]
+    if ws is None:
+        ws, _ = workspace(0, fmt, M, N, K, block_len, split_k, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    kq_gemv(fmt, packed, N, K, x, M, block_len, signs, split_k, y, ws, ws.numel(), stream)
+    return y
+
+
+def gemm(packed, N: int, K: int, x, block_len: int, signs=None, ws=None, y=None, stream=None):
+    import torch
+    M = x.shape[0]
+    if ws is None:
+        ws, _ = workspace(1, KQ_FMT_PQ2_0, M, N, K, block_len, 0, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    kq_gemm(KQ_FMT_PQ2_0, packed, N, K, x, _dtype_code(x), M, block_len, signs, y, ws,
+            ws.numel(), stream)
+    return y

@@ -1,0 +1,60 @@
+// kq_launch.h -- host-side launch entry points between the C ABI (api.cpp)
+// and the kernels.  Shapes reaching these functions are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+constexpr int kFmtPQ2 = 1;
+constexpr int kFmtQ8 = 2;
+
+inline int group_of(int fmt) { return fmt == kFmtPQ2 ? 128 : 32; }
+
+// Planar packed buffer: qs plane, then the fp16 d plane at a 256-B boundary.
+struct PlanarView {
+  uint8_t* qs;
+  uint8_t* d;
+  int64_t qs_bytes;    // N * K/4 (PQ2_0) or N * K (Q8_0)
+  int64_t row_bytes;   // qs bytes per row
+  int64_t d_per_row;   // scales per row
+  int64_t total_bytes;
+};
+
+inline PlanarView planar_view(int fmt, int64_t N, int64_t K, void* base) {
+  PlanarView v;
+  v.row_bytes = fmt == kFmtPQ2 ? K / 4 : K;
+  v.qs_bytes = N * v.row_bytes;
+  int64_t d_off = (v.qs_bytes + 255) / 256 * 256;
+  v.d_per_row = K / group_of(fmt);
+  v.total_bytes = d_off + N * v.d_per_row * 2;
+  v.qs = (uint8_t*)base;
+  v.d = (uint8_t*)base + d_off;
+  return v;
+}
+
+// All return 0 on success, -1 if the HIP runtime rejected a launch.
+int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed, hipStream_t st);
+int launch_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W, hipStream_t st);
+int launch_hadamard(const void* x, int x_bf16, void* xr, int xr_bf16, int64_t M, int64_t K,
+                    int n, const int8_t* signs, hipStream_t st);
+
+// GEMV plan: how K is split and how rows map to waves.
+struct GemvPlan {
+  int split;          // S >= 1 K-ranges
+  int rows_per_wave;  // contiguous rows owned by one wave
+  int grid_x;         // workgroups along the rows
+  int lds_bytes;      // dynamic LDS per workgroup
+};
+GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int split_req);
+int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req);
+int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,
+                int block_len, const int8_t* signs, int split_req, float* y, void* ws,
+                hipStream_t st);
+
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
+                             const void* signs_hint);
+int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_bf16, int64_t M,
+                int block_len, const int8_t* signs, float* y, void* ws, hipStream_t st);
+
+}  // namespace kq

@@ -1,0 +1,153 @@
+// pack.hip -- PQ2_0 / Q8_0 quantizers and dequantizers (planar layout).
+//
+// PQ2_0 (Bonsai 2 27B ternary g128 page, sec. 3.1): per 128-group
+// d = max|w| stored as fp16, q = round(w/d) + 1, element j in byte j/4 at bit
+// offset 2(j%4).  Q8_0 (Kipp architecture page, "Weight quantization"):
+// per 32-group the scale max|w|/127 stored as fp16, q = round(w/scale)
+// against the fp16-rounded scale.  Rounding is half away from zero, the
+// division is the IEEE one, and an all-zero group keeps d = 0 with the
+// neutral code (1 for PQ2_0, 0 for Q8_0).
+//
+// Launch shape: one thread per 32-bit word of the qs plane.  For PQ2_0 a
+// word holds 16 codes and 8 consecutive threads cover one 128-group; for
+// Q8_0 a word holds 4 int8 and 8 threads cover one 32-group.  The group max
+// is reduced across those 8 lanes with xor shuffles, so one pass reads W once
+// with coalesced 64/16-byte loads and writes the plane with coalesced dwords.
+#include "kq_device.h"
+#include "kq_launch.h"
+
+namespace kq {
+
+__device__ __forceinline__ float group8_max(float a) {
+  // the 8 lanes of a group are aligned to 8 within the wave
+  a = fmaxf(a, __shfl_xor(a, 1, 8));
+  a = fmaxf(a, __shfl_xor(a, 2, 8));
+  a = fmaxf(a, __shfl_xor(a, 4, 8));
+  return a;
+}
+
+__global__ __launch_bounds__(256) void pack_pq2_kernel(
+    const float* __restrict__ W, uint32_t* __restrict__ qs, uint16_t* __restrict__ dplane,
+    int64_t n_words) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool live = g < n_words;
+  float w[16];
+  if (live) {
+    const float4* src = reinterpret_cast<const float4*>(W) + g * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 v = src[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(w[i]));
+  amax = group8_max(amax);
+  uint16_t d16 = f32_to_f16_bits(amax);
+  float dF = f16_bits_to_f32(d16);
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    int q = 1;
+    if (dF != 0.f) {
+      q = (int)roundf(w[j] / dF) + 1;  // IEEE division, ties away from zero
+      q = q < 0 ? 0 : (q > 2 ? 2 : q);
+    }
+    word |= (uint32_t)q << (2 * j);
+  }
+  if (live) {
+    qs[g] = word;
+    if ((g & 7) == 0) dplane[g >> 3] = d16;
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_q8_kernel(
+    const float* __restrict__ W, uint32_t* __restrict__ qs, uint16_t* __restrict__ dplane,
+    int64_t n_words) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool live = g < n_words;
+  float4 v = live ? reinterpret_cast<const float4*>(W)[g] : make_float4(0.f, 0.f, 0.f, 0.f);
+  float w[4] = {v.x, v.y, v.z, v.w};
+  float amax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
+  amax = group8_max(amax);
+  float d32 = amax / 127.0f;  // IEEE division
+  uint16_t d16 = f32_to_f16_bits(d32);
+  float dF = f16_bits_to_f32(d16);
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int q = 0;
+    if (dF != 0.f) {
+      q = (int)roundf(w[j] / dF);
+      q = q < -127 ? -127 : (q > 127 ? 127 : q);
+    }
+    word |= ((uint32_t)q & 0xFFu) << (8 * j);
+  }
+  if (live) {
+    qs[g] = word;
+    if ((g & 7) == 0) dplane[g >> 3] = d16;
+  }
+}
+
+// Dequantize: one thread per 32-bit qs word.
+__global__ __launch_bounds__(256) void unpack_pq2_kernel(
+    const uint32_t* __restrict__ qs, const uint16_t* __restrict__ dplane,
+    float* __restrict__ W, int64_t n_words) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_words) return;
+  uint32_t word = qs[g];
+  float d = f16_bits_to_f32(dplane[g >> 3]);
+  float4* dst = reinterpret_cast<float4*>(W) + g * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (float)((int)((word >> (2 * (4 * i + j))) & 3u) - 1) * d;
+    dst[i] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_q8_kernel(
+    const uint32_t* __restrict__ qs, const uint16_t* __restrict__ dplane,
+    float* __restrict__ W, int64_t n_words) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_words) return;
+  uint32_t word = qs[g];
+  float d = f16_bits_to_f32(dplane[g >> 3]);
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = d * (float)(int8_t)(word >> (8 * j));
+  reinterpret_cast<float4*>(W)[g] = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+static int blocks_for(int64_t n) { return (int)((n + 255) / 256); }
+
+int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed,
+                hipStream_t st) {
+  PlanarView pv = planar_view(fmt, N, K, packed);
+  int64_t n_words = pv.qs_bytes / 4;
+  if (n_words == 0) return 0;
+  if (fmt == 1)
+    pack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words);
+  else
+    pack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W,
+                  hipStream_t st) {
+  PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
+  int64_t n_words = pv.qs_bytes / 4;
+  if (n_words == 0) return 0;
+  if (fmt == 1)
+    unpack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words);
+  else
+    unpack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace kq

@@ -1,0 +1,166 @@
+/*
+ * kq.h -- quantized-weight GEMV / GEMM for AMD MI355X (gfx950): the C ABI.
+ *
+ * What is computed (the pages this library follows):
+ *   [BT] "Bonsai 2 27B -- ternary g128 + blockwise Hadamard: the packing
+ *        contract for a Core AI port" (Core AI model zoo knowledge page)
+ *        sec. 3.1  PQ2_0 block, quantizer d = max|w|, q = round(w/d) + 1,
+ *                  code q -> (q-1)*d, and the "word view" of the codes;
+ *        sec. 4.1  R = (1/sqrt(n)) H_n S, Sylvester natural order,
+ *                  applied block-diagonally along K;
+ *        sec. 4.2  runtime order of a folded linear: sign flip, blockwise
+ *                  transform, then the ternary product y = W' (R x).
+ *   [KA] "Kipp architecture" page, "Weight quantization": Q8_0, 32-weight
+ *        blocks with one fp16 scale, quantized against the fp16-rounded
+ *        scale; decode kernels for one token, tiled matrix kernels for
+ *        prompts.
+ *   [KB] "Kipp Benchmarks" page: Q8_0 dequantization d*q; the dequantize-
+ *        once-per-tile prefill kernels ("Quantized projections on the
+ *        tensor units").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer owned by the caller
+ *   (for example PyTorch tensors).  The library never allocates, frees,
+ *   copies to or from the host, or synchronises; it only enqueues kernels on
+ *   `stream` (a hipStream_t passed as void*; NULL is the default stream) and
+ *   returns.  Results are ready when the stream reaches that point.
+ * Layouts.  Row-major, last index contiguous:  W [N][K],  x and x' [M][K],
+ *   y [M][N].  N counts output rows, K is the reduction (the page's "ne
+ *   order, K first").
+ * Packed weights (planar device layout).  kq_packed_bytes(fmt, N, K) bytes:
+ *     qs plane : the 32 code bytes of every block, row-major, blocks in K
+ *                order -- [N][K/4] bytes for PQ2_0, [N][K] int8 for Q8_0.
+ *                For PQ2_0, reading 4 bytes as a little-endian u32 gives
+ *                word i of a row holding element 16*i + j at bits 2*j
+ *                ([BT] 3.1 "Word view").
+ *     d plane  : at byte offset round_up(qs plane size, 256): one IEEE
+ *                binary16 scale per block, [N][K/128] (PQ2_0) or [N][K/32]
+ *                (Q8_0), little endian.
+ *   This is a lossless re-arrangement of the GGUF-style array of 34-byte
+ *   blocks { fp16 d; uint8 qs[32] }: only the scales move out.
+ * Alignment.  All pointers must be 16-byte aligned, else KQ_EALIGN.
+ * Errors.  Arguments are validated before anything is enqueued; on any
+ *   error nothing is launched and no output byte is written.  A failed
+ *   launch returns KQ_EDEVICE.  No HIP type or HIP error code crosses this
+ *   interface.  Contents of device memory (finite weights, sign values)
+ *   are preconditions: the library cannot read them without a sync.
+ * Threads.  No global mutable state; calls on different streams may run
+ *   concurrently.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KQ_FMT_PQ2_0 = 1, /* 128 weights: fp16 d + 32 B of 2-bit codes (34 B) */
+    KQ_FMT_Q8_0 = 2   /* 32 weights: fp16 d + 32 int8 (34 B)              */
+} kq_format;
+
+typedef enum {
+    KQ_F32 = 0,  /* IEEE binary32 */
+    KQ_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} kq_dtype;
+
+typedef enum {
+    KQ_OK = 0,
+    KQ_EINVAL = 1,       /* NULL pointer, unknown enum, negative size      */
+    KQ_ESHAPE = 2,       /* K, N, M, block_len or split_k out of contract  */
+    KQ_EALIGN = 3,       /* a pointer is not 16-byte aligned               */
+    KQ_EWORKSPACE = 4,   /* workspace missing or smaller than required     */
+    KQ_EUNSUPPORTED = 5, /* valid but unsupported combination              */
+    KQ_EDEVICE = 6       /* the HIP runtime rejected a launch              */
+} kq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kq_status_string(kq_status s);
+
+/* Bytes of the planar packed buffer for an N x K matrix in `fmt`, or 0 if
+ * the shape is invalid (K % 128 for PQ2_0, K % 32 for Q8_0, N >= 1). */
+size_t kq_packed_bytes(kq_format fmt, int64_t N, int64_t K);
+
+/* PQ2_0 quantizer, [BT] 3.1.  For every row n and 128-group of W [N][K]
+ * (fp32): d16 = fp16_rne(max|w|), and for each weight
+ * q = round_half_away(w / f32(d16)) + 1 in {0,1,2} with IEEE fp32 division
+ * (q = 1 for every weight of a group whose d16 is 0).  Writes the planar
+ * buffer `packed` (kq_packed_bytes(KQ_FMT_PQ2_0, N, K) bytes); the bytes
+ * are deterministic.  Precondition: W finite with max|w| < 65520 per group.
+ * Errors: KQ_EINVAL (NULL), KQ_ESHAPE (N < 1, K < 128, K % 128),
+ * KQ_EALIGN. */
+kq_status kq_pack_pq2(const float *W, int64_t N, int64_t K, void *packed,
+                      void *stream);
+
+/* Q8_0 quantizer, [KA].  Per 32-group: d32 = max|w| / 127 (fp32 division),
+ * d16 = fp16_rne(d32); q = round_half_away(w / f32(d16)) clamped to
+ * [-127, 127] (q = 0 when d16 is 0).  Writes the planar buffer.
+ * Errors as kq_pack_pq2, with K % 32. */
+kq_status kq_pack_q8(const float *W, int64_t N, int64_t K, void *packed,
+                     void *stream);
+
+/* Dequantize a planar buffer to fp32 W_out [N][K]: (q-1)*d for PQ2_0 (a
+ * foreign code 3 decodes to 2*d), d*q for Q8_0 ([BT] 3.1, [KB]).  Exact.
+ * Errors: KQ_EINVAL, KQ_ESHAPE, KQ_EALIGN. */
+kq_status kq_unpack(kq_format fmt, const void *packed, int64_t N, int64_t K,
+                    float *W_out, void *stream);
+
+/* Blockwise rotation x' = (1/sqrt(n)) H_n (s (.) x) of every n-block of
+ * every row of x [M][K], [BT] 4.1-4.2 (sign first, then the transform; H_n
+ * Sylvester natural order).  n = block_len in {1, 2, 4, ..., 1024}, n | K,
+ * and K % 16 == 0.  signs: K int8 entries (negative -> -1, else +1) or NULL
+ * for all +1.  x_dt / xr_dt: KQ_F32 or KQ_BF16 (arithmetic in fp32, one
+ * round-to-nearest-even to bf16 at the store when xr_dt is KQ_BF16).  x and
+ * xr may not overlap.  Errors: KQ_EINVAL, KQ_ESHAPE, KQ_EALIGN. */
+kq_status kq_hadamard_blocks(const void *x, kq_dtype x_dt, void *xr,
+                             kq_dtype xr_dt, int64_t M, int64_t K,
+                             int32_t block_len, const int8_t *signs,
+                             void *stream);
+
+/* Workspace bytes kq_gemv (op = 0) or kq_gemm (op = 1) needs for these
+ * arguments; 0 means none.  split_k as for kq_gemv (0 = automatic). */
+size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N,
+                          int64_t K, int32_t block_len, int32_t split_k);
+
+/* Quantized GEMV for M in 1..8 activation rows (one decode step, or a few
+ * sequences sharing the weights):
+ *     y[m][n] = sum_k deq(W)[n][k] * x'[m][k],   x' = rotation of x
+ * with deq as in kq_unpack and x' as in kq_hadamard_blocks (block_len 0:
+ * x' = x (.) s, no transform).  x is fp32 [M][K]; y is fp32 [M][N].
+ * Arithmetic: x' in fp32, codes decoded exactly, fp32 accumulation; each
+ * output is within 1e-3 * sum_k |deq(W)[n][k] x'[m][k]| of the exact value.
+ * split_k: 1 = one pass over K; S > 1 splits K into S contiguous ranges of
+ * whole blocks whose fp32 partial sums are added in ascending order
+ * (deterministic, no atomics); 0 = chosen by the library.  Results are
+ * bitwise reproducible for a given (split_k, M, N, K).
+ * workspace: at least kq_workspace_bytes(0, ...) bytes of device memory
+ * (x' and split partials), or NULL when that is 0.
+ * Errors: KQ_EINVAL, KQ_ESHAPE (M not in 1..8, N < 1, K not a multiple of
+ * the block, bad block_len, split_k < 0 or larger than K's block count),
+ * KQ_EALIGN, KQ_EWORKSPACE, KQ_EDEVICE. */
+kq_status kq_gemv(kq_format fmt, const void *packed, int64_t N, int64_t K,
+                  const float *x, int64_t M, int32_t block_len,
+                  const int8_t *signs, int32_t split_k, float *y,
+                  void *workspace, size_t ws_bytes, void *stream);
+
+/* Prefill GEMM (many tokens) for PQ2_0 weights, dequantize-once-per-tile
+ * ([KB] "Quantized projections on the tensor units"; [BT] 8.3 tiled GEMM):
+ *     y[m][n] = sum_k bf16(deq(W)[n][k]) * bf16(x'[m][k])   (fp32 accumulate)
+ * x is [M][K] in x_dt (KQ_BF16 or KQ_F32); x' is rounded once to bf16;
+ * y is fp32 [M][N].  Each output is within 1e-2 * sum_k |deq(W) x'| of the
+ * exact value.  M >= 1, N >= 1, K % 128 == 0.  workspace: at least
+ * kq_workspace_bytes(1, ...) bytes (the bf16 x').
+ * Errors: as kq_gemv; KQ_EUNSUPPORTED for fmt other than KQ_FMT_PQ2_0. */
+kq_status kq_gemm(kq_format fmt, const void *packed, int64_t N, int64_t K,
+                  const void *x, kq_dtype x_dt, int64_t M, int32_t block_len,
+                  const int8_t *signs, float *y, void *workspace,
+                  size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KQ_H */

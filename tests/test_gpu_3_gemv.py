@@ -1,0 +1,190 @@
+"""GPU parity of kq_gemv against the CPU oracle.
+
+Acceptance (per output): |y_gpu - y_ref| <= 1e-3 * sum_k |deq(W)[n][k] x'[m][k]|
+with y_ref and the bound from the oracle in binary64.  The oracle packs the
+weights itself (from the same seeded fp32 W); the GPU path uses its own
+packed bytes (bit-exactness of the two packers is tested separately).
+Integer-exact cases (block_len 0, power-of-two scales, small integer
+activations) must match with tolerance 0, including under split-K."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_kq_gemv_amd import inputs
+from tests._gpu import assert_within_bound, check_guard, dev, gpu, guarded_empty, host, need_gpu
+
+pytestmark = gpu
+TOL = 1e-3
+
+
+@pytest.fixture(autouse=True)
+def _need():
+    need_gpu()
+
+
+def _kq():
+    import gemm_kq_gemv_amd as kq
+    return kq
+
+
+def _oracle_ref(fmt, W, x, block_len, signs=None):
+    N, K = W.shape
+    aos = oracle.pack_pq2_aos(W) if fmt == 1 else oracle.pack_q8_aos(W)
+    return oracle.gemv_aos(fmt, aos, N, K, x, block_len, signs)
+
+
+def _run(fmt, W, x, block_len, signs=None, split_k=0, packed=None):
+    kq = _kq()
+    N, K = W.shape
+    M = x.shape[0]
+    if packed is None:
+        packed = kq.pack(fmt, dev(W))
+    y, buf = guarded_empty((M, N))
+    kq.gemv(fmt, packed, N, K, dev(x), block_len, None if signs is None else dev(signs),
+            split_k, y=y)
+    out = host(y)
+    check_guard(buf, M * N)
+    return out
+
+
+# ---- the configurations ------------------------------------------------------
+
+def test_c1_pq2_k512_n1024():
+    W = inputs.weights(1001, 1024, 512)
+    x = inputs.activations(2001, 1, 512)
+    y_ref, b = _oracle_ref(1, W, x, 128)
+    assert_within_bound(_run(1, W, x, 128), y_ref, b, TOL, "C1")
+
+
+def test_c2_pq2_k5120_n10240():
+    W = inputs.weights(1002, 10240, 5120)
+    x = inputs.activations(2002, 1, 5120)
+    y_ref, b = _oracle_ref(1, W, x, 128)
+    assert_within_bound(_run(1, W, x, 128), y_ref, b, TOL, "C2")
+
+
+@pytest.fixture(scope="module")
+def c3_inputs():
+    kq = _kq()
+    N, K = 248320, 5120
+    W = inputs.weights(1003, N, K)
+    Wd = dev(W)
+    packed = kq.pack(1, Wd)
+    del Wd
+    torch.cuda.empty_cache()
+    return W, packed
+
+
+@pytest.mark.parametrize("split_k", [2, 4])
+def test_c3_pq2_lm_head_full_size_sampled(split_k, c3_inputs):
+    """N = 248320 on the GPU, checked on 1500 sampled rows (plus the ends)."""
+    N, K = 248320, 5120
+    W, packed = c3_inputs
+    x = inputs.activations(2003, 1, K)
+    y = _run(1, W, x, 128, split_k=split_k, packed=packed)
+    rows = np.unique(np.concatenate([inputs.rng(5).integers(0, N, 1500), [0, 1, N - 2, N - 1]]))
+    y_ref, b = _oracle_ref(1, W[rows], x, 128)
+    assert_within_bound(y[:, rows], y_ref, b, TOL, f"C3 split {split_k}")
+    # the GPU-packed bytes of the sampled rows are the oracle's
+    want = oracle.aos_to_planar(1, oracle.pack_pq2_aos(W[rows]), len(rows), K)
+    got = host(packed)
+    assert np.array_equal(got[:N * K // 4].reshape(N, K // 4)[rows], want[:len(rows) * K // 4].reshape(-1, K // 4))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_c4_q8_k5120_n17408(M):
+    W = inputs.weights(1004, 17408, 5120)
+    x = inputs.activations(2004, M, 5120)
+    y_ref, b = _oracle_ref(2, W, x, 0)
+    assert_within_bound(_run(2, W, x, 0), y_ref, b, TOL, f"C4 M={M}")
+
+
+# ---- coverage of shapes, M, split-K, signs -----------------------------------
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 6, 7, 8])
+def test_all_m(fmt, M):
+    N, K = 300, 2048
+    W = inputs.weights(400 + M, N, K)
+    x = inputs.activations(500 + M, M, K, offset=0.5)
+    bl = 128 if fmt == 1 else 0
+    y_ref, b = _oracle_ref(fmt, W, x, bl)
+    assert_within_bound(_run(fmt, W, x, bl), y_ref, b, TOL, f"fmt {fmt} M {M}")
+
+
+@pytest.mark.parametrize("fmt,N,K", [(1, 1, 128), (1, 5, 256), (1, 67, 384), (1, 129, 640),
+                                     (1, 1000, 6144), (1, 33, 17408), (2, 1, 32), (2, 3, 96),
+                                     (2, 71, 1056), (2, 257, 4096)])
+def test_ragged_shapes(fmt, N, K):
+    W = inputs.weights(600 + N, N, K)
+    x = inputs.activations(601 + N, 2, K, offset=-0.25)
+    bl = 128 if (fmt == 1 and K % 128 == 0) else 32
+    s = inputs.signs(602, K)
+    y_ref, b = _oracle_ref(fmt, W, x, bl, s)
+    assert_within_bound(_run(fmt, W, x, bl, s), y_ref, b, TOL, f"{fmt} {N}x{K}")
+
+
+@pytest.mark.parametrize("block_len", [0, 2, 64, 256, 1024])
+def test_block_lengths(block_len):
+    N, K = 256, 5120
+    W = inputs.weights(700, N, K)
+    x = inputs.activations(701, 1, K)
+    s = inputs.signs(702, K) if block_len in (0, 1024) else None
+    y_ref, b = _oracle_ref(1, W, x, block_len, s)
+    assert_within_bound(_run(1, W, x, block_len, s), y_ref, b, TOL, f"n={block_len}")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("split_k", [1, 2, 3, 5, 40])
+def test_split_k(fmt, split_k):
+    N, K = 777, 5120
+    W = inputs.weights(800, N, K)
+    x = inputs.activations(801, 2, K)
+    bl = 128 if fmt == 1 else 0
+    y_ref, b = _oracle_ref(fmt, W, x, bl)
+    assert_within_bound(_run(fmt, W, x, bl, split_k=split_k), y_ref, b, TOL, f"S={split_k}")
+
+
+def test_deterministic_run_to_run():
+    kq = _kq()
+    N, K = 10240, 5120
+    W = inputs.weights(900, N, K)
+    x = dev(inputs.activations(901, 1, K))
+    packed = kq.pack(1, dev(W))
+    for split_k in (1, 4):
+        a = host(kq.gemv(1, packed, N, K, x, 128, split_k=split_k))
+        b = host(kq.gemv(1, packed, N, K, x, 128, split_k=split_k))
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---- integer-exact, tolerance 0 ----------------------------------------------
+
+@pytest.mark.parametrize("N,K,M", [(1, 128, 1), (37, 384, 2), (300, 5120, 1), (65, 17408, 3)])
+@pytest.mark.parametrize("split_k", [1, 3])
+def test_integer_exact_pq2(N, K, M, split_k):
+    W = inputs.ternary_exact_weights(1100 + N, N, K, exp2=3)
+    x = inputs.integer_activations(1101 + N, M, K, lim=64)
+    y_ref, _ = _oracle_ref(1, W, x, 0)
+    y = _run(1, W, x, 0, split_k=split_k)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 32, 1), (45, 160, 4), (300, 5120, 8)])
+@pytest.mark.parametrize("split_k", [1, 2])
+def test_integer_exact_q8(N, K, M, split_k):
+    W = inputs.int8_exact_weights(1200 + N, N, K, exp2=7)
+    x = inputs.integer_activations(1201 + N, M, K, lim=8)
+    y_ref, _ = _oracle_ref(2, W, x, 0)
+    y = _run(2, W, x, 0, split_k=split_k)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_all_plus_one_rows_closed_form():
+    # every code 2 with d = 1 and no signs: y = sum_b sqrt(n) x[b n]
+    N, K, n = 64, 1024, 128
+    W = np.ones((N, K), np.float32)
+    x = inputs.activations(1300, 1, K)
+    y = _run(1, W, x, n)
+    want = np.sqrt(n) * x[0, ::n].astype(np.float64).sum()
+    assert np.allclose(y[0], want, rtol=1e-5, atol=1e-5)
