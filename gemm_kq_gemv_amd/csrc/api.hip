@@ -109,8 +109,7 @@ kq_status kq_gemv(kq_format fmt, const void* packed, int64_t N, int64_t K, const
   kq::GemvPlan plan = kq::plan_gemv(fmt, M, N, K, split_k);
   if (plan.split < 1) return KQ_EUNSUPPORTED;  // split_k too small for the LDS budget
   const int64_t need = kq::gemv_workspace_bytes(fmt, M, N, K, block_len, split_k);
-  const bool uses_ws = block_len > 0 || signs || plan.split > 1;
-  if (uses_ws && (!workspace || (int64_t)ws_bytes < need)) return KQ_EWORKSPACE;
+  if (need > 0 && (!workspace || (int64_t)ws_bytes < need)) return KQ_EWORKSPACE;
   const int rc = kq::launch_gemv(fmt, packed, N, K, x, M, block_len, signs, split_k, y, workspace,
                                  as_stream(stream));
   return rc == -2 ? KQ_EUNSUPPORTED : launched(rc);

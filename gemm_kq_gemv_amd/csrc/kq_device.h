@@ -58,4 +58,35 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Sum over each aligned group of n lanes (n in {2, 4, 8, 16, 32}); every lane
+// of a group receives its group's total.
+__device__ __forceinline__ float group_sum_pow2(float v, int n) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  if (n >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  if (n >= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  if (n >= 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+  if (n >= 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+// Raw buffer access (gfx9 buffer resource, stride 0): loads whose byte offset
+// lies outside [0, num_bytes) return zero instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;  // an offset past any range used here
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load_16B(BufRsrc r, uint32_t off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t buffer_load_2B(BufRsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 }  // namespace kq

@@ -51,9 +51,13 @@ def test_packed_bytes_layout(oracle_lib):
 
 def test_workspace_sizes():
     kq = _lib()
-    # x' (fp32, 256-aligned) and, with split-K, S*M*N partials
-    assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 128, 1) == 20480
-    assert kq.kq_workspace_bytes(0, 1, 1, 248320, 5120, 128, 2) == 20480 + 2 * 248320 * 4
+    # the rotation runs in the GEMV prologue: no workspace without split-K
+    assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 128, 1) == 0
+    assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 128, 0) == 0
+    # split-K: S*M*N fp32 partials
+    assert kq.kq_workspace_bytes(0, 1, 1, 248320, 5120, 128, 2) == 2 * 248320 * 4
+    # n = 1024 blocks cut by a K-slice boundary (13 * 128): x' pre-pass + partials
+    assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 1024, 3) == 20480 + 3 * 10240 * 4
     assert kq.kq_workspace_bytes(1, 1, 2048, 10240, 5120, 128, 0) == 2048 * 5120 * 2
     assert kq.kq_workspace_bytes(0, 1, 9, 64, 128, 0, 0) == 0   # M > 8
     assert kq.kq_workspace_bytes(0, 1, 1, 64, 100, 0, 0) == 0   # bad K
@@ -124,12 +128,15 @@ def test_gemv_rejections():
     assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 128, None, 3, FAKE, FAKE, ws, 0) == "KQ_ESHAPE"
     assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 128, None, -1, FAKE, FAKE, ws, 0) == "KQ_ESHAPE"
     assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 128, None, 0, MISALIGNED, FAKE, ws, 0) == "KQ_EALIGN"
-    assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 128, None, 0, FAKE, None, 0, 0) == "KQ_EWORKSPACE"
-    assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 128, None, 0, FAKE, FAKE, 64, 0) == "KQ_EWORKSPACE"
-    # split-K needs its partial buffer too
+    # split-K needs its partial buffer
     need = kq.kq_workspace_bytes(0, 1, 1, 64, 256, 0, 2)
-    assert need == 256 * 4 + 2 * 64 * 4        # x' (M*K*4) + S*M*N*4 partials
-    assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 0, None, 2, FAKE, FAKE, 256, 0) == "KQ_EWORKSPACE"
+    assert need == 2 * 64 * 4                  # S*M*N*4 partials
+    assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 0, None, 2, FAKE, None, 0, 0) == "KQ_EWORKSPACE"
+    assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 0, None, 2, FAKE, FAKE, need - 4, 0) == "KQ_EWORKSPACE"
+    # a 1024-block cut by a slice boundary needs the x' pre-pass buffer too
+    need = kq.kq_workspace_bytes(0, 1, 1, 64, 5120, 1024, 3)
+    assert need == 5120 * 4 + 3 * 64 * 4
+    assert _status(g, 1, FAKE, 64, 5120, FAKE, 1, 1024, None, 3, FAKE, FAKE, 3 * 64 * 4, 0) == "KQ_EWORKSPACE"
 
 
 @pytest.mark.usefixtures("nogpu")

@@ -160,8 +160,9 @@ def test_deterministic_run_to_run():
 
 # ---- integer-exact, tolerance 0 ----------------------------------------------
 
-@pytest.mark.parametrize("N,K,M", [(1, 128, 1), (37, 384, 2), (300, 5120, 1), (65, 17408, 3)])
-@pytest.mark.parametrize("split_k", [1, 3])
+@pytest.mark.parametrize("N,K,M,split_k", [(1, 128, 1, 1), (37, 384, 2, 1), (37, 384, 2, 3),
+                                           (300, 5120, 1, 1), (300, 5120, 1, 3),
+                                           (65, 17408, 3, 0), (65, 17408, 3, 7)])
 def test_integer_exact_pq2(N, K, M, split_k):
     W = inputs.ternary_exact_weights(1100 + N, N, K, exp2=3)
     x = inputs.integer_activations(1101 + N, M, K, lim=64)
@@ -170,14 +171,31 @@ def test_integer_exact_pq2(N, K, M, split_k):
     assert np.array_equal(y.astype(np.float64), y_ref)
 
 
-@pytest.mark.parametrize("N,K,M", [(1, 32, 1), (45, 160, 4), (300, 5120, 8)])
-@pytest.mark.parametrize("split_k", [1, 2])
+@pytest.mark.parametrize("N,K,M,split_k", [(1, 32, 1, 1), (45, 160, 4, 1), (45, 160, 4, 2),
+                                           (300, 5120, 8, 0), (300, 5120, 8, 8)])
 def test_integer_exact_q8(N, K, M, split_k):
     W = inputs.int8_exact_weights(1200 + N, N, K, exp2=7)
     x = inputs.integer_activations(1201 + N, M, K, lim=8)
     y_ref, _ = _oracle_ref(2, W, x, 0)
     y = _run(2, W, x, 0, split_k=split_k)
     assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_infeasible_split_is_rejected_without_writing():
+    kq = _kq()
+    N, K = 64, 5120
+    W = inputs.weights(1250, N, K)
+    packed = kq.pack(1, dev(W))
+    x = dev(inputs.activations(1251, 8, K))
+    ws, nws = kq.workspace(0, 1, 8, N, K, 0, 0)
+    y, buf = guarded_empty((8, N))
+    y.fill_(-1.0)
+    for split_k, status in ((1, "KQ_EUNSUPPORTED"), (41, "KQ_ESHAPE")):
+        with pytest.raises(kq.KQError) as e:
+            kq.kq_gemv(1, packed, N, K, x, 8, 0, None, split_k, y, ws, nws)
+        assert e.value.name == status
+    assert np.all(host(y) == -1.0)
+    check_guard(buf, 8 * N)
 
 
 def test_all_plus_one_rows_closed_form():
@@ -187,4 +205,5 @@ def test_all_plus_one_rows_closed_form():
     x = inputs.activations(1300, 1, K)
     y = _run(1, W, x, n)
     want = np.sqrt(n) * x[0, ::n].astype(np.float64).sum()
-    assert np.allclose(y[0], want, rtol=1e-5, atol=1e-5)
+    bound = np.abs(oracle.rotate(x.astype(np.float64), n)).sum()   # sum_k |W x'| with W = 1
+    assert np.all(np.abs(y[0] - want) <= TOL * bound)
