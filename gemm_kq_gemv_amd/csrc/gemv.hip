@@ -1,474 +1,753 @@
-// gemv.hip -- quantized GEMV (M = 1..8 activation rows), PQ2_0 and Q8_0.
+// gemv.hip -- quantized GEMV (M = 1..8 activation rows) on the CDNA4 matrix cores.
 //
 // y[m][n] = sum_k deq(W)[n][k] * x'[m][k],   x' = blockwise rotation of x
 //   PQ2_0 deq = (q-1)*d per 128-group (Bonsai ternary g128 page, sec. 3.1);
-//   Q8_0  deq = d*q per 32-group (Kipp pages);
+//   Q8_0  deq = d*q per 32-group (Kipp pages, "Weight quantization");
 //   x' = (1/sqrt(n)) H_n (s (.) x) per n-block (Bonsai page, sec. 4.1-4.2).
 //
 // gfx950 design
 // -------------
-// * One launch.  Every workgroup (8 waves, one per CU) first turns its
-//   K-range of x into x' in LDS -- sign flip, in-register and cross-lane
-//   butterflies, 1/sqrt(n) -- so the rotation costs no extra kernel launch
-//   and x' never goes through memory.
-// * Work unit.  A row of the qs plane is cut into 16-byte chunks (64 PQ2_0
-//   codes or 16 Q8_0 weights; half a quantization group each, so a chunk has
-//   one scale).  A wave owns a contiguous run of rows and walks them in
-//   batches of RB rows.  One "step" loads one chunk per lane for each of the
-//   RB rows: lane l takes chunk p*64 + l, so each load instruction is a
-//   coalesced 1 KiB dwordx4 read of one row.  The T chunks left when a row is
-//   not a multiple of 64 chunks form a tail step in which the wave splits
-//   into G = 64/T lane groups, one row each.
-// * Loads.  Buffer loads whose resource covers exactly the batch's rows: rows
-//   past the batch or past N and the idle lanes of a tail step read zeros
-//   from the hardware range check, so the loads need no branches and the
-//   loads of step s+2 stay in flight while step s is computed (three
-//   rotating register buffers).  Every SIMD gets the same number of rows.
-// * PQ2_0 arithmetic.  x' is staged as fp16 pairs: each 128-element group of
-//   x' is scaled by a power of two that puts its largest magnitude in
-//   [2^14, 2^15) (the inverse is folded into the weight scale), then rounded
-//   once to fp16 -- the activation precision of the pages' own matvec
-//   kernels -- so each product is exact to 2^-11 relative and the result
-//   stays within 2^-11 * sum|W x'| plus fp32 accumulation error.
-//   (w & 0x33333333) and ((w >> 2) & 0x33333333) leave one 2-bit code per
-//   nibble; the gfx950 fp4 converter turns two nibbles into an exact fp16
-//   pair (scale 2 gives the code c), and v_dot2_f32_f16 multiplies it with
-//   the matching x' pair, accumulating in fp32: 16 codes cost 3 bit ops +
-//   8 conversions + 8 dot products.  The ternary map's -1 is folded into a
-//   per-chunk sum X of the same fp16 values:
-//   sum (c-1) x' = sum c x' - X   (the Bonsai page, sec. 8.5, folds the -1
-//   the same way).
-// * Q8_0 arithmetic.  x' stays fp32; each int8 is converted with a
-//   sign-extending byte select and multiplied with an fp32 FMA.
-// * Reduction.  Per row, the 64 lane partials are summed with DPP row
-//   reductions plus four lane reads (fixed order, deterministic); tail-step
-//   partials go through a small per-wave LDS scratch and are summed by the
-//   row's owning lane in lane order.  No atomics.
-// * Split-K.  blockIdx.y selects one of S contiguous ranges of whole groups;
-//   each range writes fp32 partials [S][M][N] that a second kernel adds in
-//   ascending s.
+// The product is bandwidth-bound, so the arithmetic has to stay well under
+// one vector instruction per weight.  The multiply-adds go to the matrix
+// cores and the vector ALUs only unpack:
+// * PQ2_0.  A 2-bit code c masked into the low bits of a nibble IS an E2M1
+//   (fp4) number equal to c/2, so (w & 0x33333333) and ((w >> 2) &
+//   0x33333333) turn one 32-bit word into 16 fp4 operands with three bit
+//   operations.  v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 weight rows
+//   x 128 codes (one quantization group) by a 16-row operand that holds x' as
+//   four e5m2 terms (|x' - (t0 + t1 + t2 + t3)| <= 2^-12 |x'|) for up to four
+//   activation rows.  The ternary map's -1 is folded in with the group sum X
+//   of the same terms: sum (c-1) x' = 2 sum (c/2) x' - X (the Bonsai page,
+//   sec. 8.5, folds the -1 into an activation sum as well).  Each group of x'
+//   is scaled by its own power of two first, so its range suits e5m2.
+// * Q8_0.  Each int8 is converted to bf16 exactly and multiplied with x'
+//   split into bf16 hi + lo parts (2^-17 relative) by
+//   v_mfma_f32_16x16x32_bf16; one MFMA covers 16 weight rows x one 32-group
+//   for up to 8 activation rows.
+// * Work split.  A workgroup owns a K-slice and a range of 16-row blocks.  Its
+//   waves split the K-slice (GS groups each) and hold their part of the
+//   activation operand in registers for the whole kernel.  Every wave
+//   streams the same row blocks: one 16-byte buffer load per lane covers 16
+//   rows x 64 bytes (a pair of groups), and one permlane32 swap per register
+//   puts the pair into MFMA operand order (lane block kb ends up with bytes
+//   {0, 16, 8, 24}[kb] + 0..7 of each group; the activation operand uses the
+//   same K order).  Weight loads run D row blocks ahead of the arithmetic;
+//   the first ones are issued right after the activation loads, so the
+//   prologue overlaps the first weight fetches.  Buffer-resource range
+//   checks return zeros past the last row, so the loads need no branches.
+// * Prologue.  PQ2_0: every wave rotates and splits its own 1024-element
+//   K-range, butterflies in registers and across lanes (DPP, permlane
+//   swaps), without workgroup barriers.  Q8_0: the workgroup stages its
+//   K-slice of x in LDS (with LDS butterflies for wide rotation blocks) and
+//   each lane converts its operand from there.
+// * Reduction.  After the MFMAs each lane's accumulators belong to one
+//   (weight row, activation row); the wave partials go through LDS and are
+//   added in wave order every RBR row blocks (deterministic, no atomics).
+// * Split-K.  blockIdx.y selects one of S contiguous K-slices made of whole
+//   rotation blocks; each writes fp32 partials [S][M][N] that a second kernel
+//   adds in ascending s.
 #include "kq_device.h"
 #include "kq_launch.h"
 
 namespace kq {
 
-constexpr int kWaves = 8;  // waves per workgroup (one workgroup per CU)
-constexpr int kThreads = kWaves * 64;
-constexpr int kPadDW = 4;  // dwords of padding per staged chunk (bank spread)
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-template <int FMT>
-struct Fmt;
-template <>
-struct Fmt<kFmtPQ2> {
-  static constexpr int CW = 64;        // elements per 16-byte chunk
-  static constexpr int CHUNK_DW = 32;  // staged dwords per chunk (fp16 pairs)
-  static constexpr int XDW = 8;        // staged dwords per 32-bit weight word
-  static constexpr bool FOLD = true;
-};
-template <>
-struct Fmt<kFmtQ8> {
-  static constexpr int CW = 16;
-  static constexpr int CHUNK_DW = 16;  // fp32
-  static constexpr int XDW = 4;
-  static constexpr bool FOLD = false;
-};
-
-template <int M>
-struct RowsPerBatch {
-  static constexpr int value = M <= 2 ? 8 : (M <= 4 ? 4 : 2);
-};
+constexpr int kRB = 16;  // weight rows per block (MFMA width)
+constexpr int kLdsBudget = 160 * 1024;
+constexpr int kTargetWGs = 256;  // one workgroup per CU
 
 struct GemvArgs {
   const uint8_t* qs;
-  const uint16_t* dpl;
-  const float* x;        // activations [M][K]: raw (rotated in the prologue) or x'
-  const int8_t* signs;   // K entries applied in the prologue, or null
+  const uint8_t* dpl;
+  const float* x;        // activations [M][K]
+  const int8_t* signs;   // K entries, or null
   float* out;            // y [M][N] (S == 1) or partials [S][M][N]
   int64_t N, K;
-  int row_bytes;         // qs bytes per row
-  int d_per_row;         // scales per row
-  int n_groups;          // quantization groups per row
-  int split;             // S
-  int rows_per_wave;
-  int max_slice_chunks;  // LDS is sized for this many chunks
-  int log2n;             // butterfly stages of the prologue rotation (0: none)
-  float scale;           // 1/sqrt(n), or 1
+  uint32_t row_bytes;    // qs bytes per weight row (32 per group)
+  uint32_t d_row_bytes;  // scale bytes per weight row
+  int G;                 // groups per row
+  int U;                 // groups per rotation block (slices hold whole blocks)
+  int S;                 // K slices
+  int total_rb;          // 16-row blocks
+  int grid_x;
+  int log2n;             // rotation block length (0: no transform)
+  float inv_sqrt_n;
 };
 
-// two 2-bit codes (one per nibble of byte SEL) -> exact fp16 pair (c, c')
-template <int SEL>
-__device__ __forceinline__ f16x2 codes2h(uint32_t spread) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(spread, 2.0f, SEL);
+// ---------------------------------------------------------------------------
+// shared device helpers
+
+__device__ __forceinline__ uint2 buffer_load_8B(BufRsrc r, uint32_t off) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v.x, v.y);
 }
 
-__device__ __forceinline__ float dot2(f16x2 a, uint32_t b_bits, float c) {
-  return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2, b_bits), c, false);
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
-template <int FMT, int M>
-__global__ __launch_bounds__(kThreads, 1) void gemv_kernel(GemvArgs a) {
-  using F = Fmt<FMT>;
-  constexpr int CW = F::CW;
-  constexpr int CS = F::CHUNK_DW + kPadDW;  // staged chunk stride (dwords)
-  constexpr int RB = RowsPerBatch<M>::value;
-  extern __shared__ uint32_t lds[];
+// value of lane (lane ^ DIST), DIST in {1, 2, 4, 8, 16, 32}
+template <int DIST>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (DIST == 1) {
+    return dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+  } else if constexpr (DIST == 2) {
+    return dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (DIST == 4) {
+    return dpp<0x1B>(dpp<0x141>(v));  // half-row mirror (i^7), then quad_perm i^3
+  } else if constexpr (DIST == 8) {
+    return dpp<0x141>(dpp<0x140>(v));  // row mirror (i^15), then half-row mirror (i^7)
+  } else if constexpr (DIST == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                    false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 16) ? p[0] : p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                    false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? p[0] : p[1]);
+  }
+}
 
-  const int lane = lane_id();
-  // wave index as a scalar: everything derived from it (rows, buffer
-  // resources) stays in SGPRs
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-
-  // ---- K range of this slice (whole groups), in chunks (2 per group)
-  const int s = blockIdx.y;
-  const int g0 = (int)((int64_t)s * a.n_groups / a.split);
-  const int g1 = (int)((int64_t)(s + 1) * a.n_groups / a.split);
-  const int c0 = 2 * g0;
-  const int Cs = 2 * (g1 - g0);
-  const int Qs = Cs >> 6;   // full main passes
-  const int Ts = Cs & 63;   // tail chunks
-  const int G = Ts ? (64 / Ts) : 1;           // rows per tail load
-  const int RBt = Ts ? (RB + G - 1) / G : 0;  // tail loads per batch
-  const int steps_per_batch = Qs + (Ts ? 1 : 0);
-
-  // ---- rows of this wave
-  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + wave;
-  const int64_t r_begin = wave_id * a.rows_per_wave;
-  const int64_t r_end = r_begin + a.rows_per_wave < a.N ? r_begin + a.rows_per_wave : a.N;
-  const int n_batches = r_begin < r_end ? (int)((r_end - r_begin + RB - 1) / RB) : 0;
-  const int n_steps = n_batches * steps_per_batch;
-
-  const int MC = a.max_slice_chunks;
-  uint32_t* xs = lds;                                        // [M][MC][CS] staged x'
-  float* xsum = reinterpret_cast<float*>(lds + M * MC * CS);  // [M][MC] chunk sums X
-  float* xinv = xsum + (F::FOLD ? M * MC : 0);                // [M][MC] inverse range scale
-  float* scratch = xinv + (F::FOLD ? M * MC : 0) + wave * (RB * M * 64);  // tail partials
-
-  const int tail_row = Ts ? lane / Ts : 0;
-  const int tail_chunk = Ts ? (Qs << 6) + lane % Ts : 0;
-  const bool tail_lane = Ts ? lane < G * Ts : false;
-
-  // Weight loads: branch-free buffer loads; the resource of a batch covers
-  // exactly its rows of this K-slice.  Offsets are 32-bit: per lane a base,
-  // plus a uniform row stride per load.
-  const uint32_t rbytes = (uint32_t)a.row_bytes;
-  const uint32_t dbytes = (uint32_t)a.d_per_row * 2u;
-  // tail step: lane group tail_row takes rows tail_row, tail_row + G, ...
-  const uint32_t tq_lane = tail_lane ? (uint32_t)tail_chunk * 16u + (uint32_t)tail_row * rbytes : kOutOfRange;
-  const uint32_t td_lane = tail_lane ? (uint32_t)(tail_chunk >> 1) * 2u + (uint32_t)tail_row * dbytes : kOutOfRange;
-  auto load_step = [&](int step, uint4 (&q)[RB], uint32_t (&d)[RB]) {
-    const int b = step / steps_per_batch;
-    const int p = step - b * steps_per_batch;
-    const int64_t row0 = r_begin + (int64_t)b * RB;
-    const int rows = (int)(r_end - row0 < RB ? r_end - row0 : RB);
-    const BufRsrc rq = make_rsrc(a.qs + row0 * a.row_bytes + (int64_t)c0 * 16,
-                                 (uint32_t)(rows - 1) * rbytes + (uint32_t)Cs * 16u);
-    const BufRsrc rd = make_rsrc(a.dpl + row0 * a.d_per_row + g0,
-                                 (uint32_t)(rows - 1) * dbytes + (uint32_t)(Cs >> 1) * 2u);
-    if (p != Qs) {  // main step: lane takes chunk p*64 + lane of rows 0..RB-1
-      const uint32_t q_lane = (uint32_t)((p << 6) + lane) * 16u;
-      const uint32_t d_lane = (uint32_t)((p << 5) + (lane >> 1)) * 2u;
+// butterfly across lanes at distance DIST: the lower lane keeps a + b, the
+// upper one a - b (natural-order Sylvester stage)
+template <int DIST>
+__device__ __forceinline__ void lane_butterfly(float (&v)[16]) {
+  const float sgn = (threadIdx.x & DIST) ? -1.f : 1.f;
 #pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        q[j] = buffer_load_16B(rq, q_lane + (uint32_t)j * rbytes);
-        d[j] = buffer_load_2B(rd, d_lane + (uint32_t)j * dbytes);  // raw fp16 bits
-      }
-    } else {        // tail step: load j takes row G*j + tail_row
-#pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        const bool ok = j < RBt;
-        q[j] = buffer_load_16B(rq, ok ? tq_lane + (uint32_t)(G * j) * rbytes : kOutOfRange);
-        d[j] = buffer_load_2B(rd, ok ? td_lane + (uint32_t)(G * j) * dbytes : kOutOfRange);
-      }
+  for (int i = 0; i < 16; ++i) v[i] = fmaf(sgn, v[i], xor_lane<DIST>(v[i]));
+}
+
+// power-of-two exponent e that puts bound * 2^e in [2^14, 2^15)
+__device__ __forceinline__ int range_exponent(float bound) {
+  if (!(bound > 0.f) || !(bound < INFINITY)) return 0;
+  const int e = 14 - ilogbf(bound);
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+
+// bf16 bits (in the upper half of a binary32) of an int8 byte: exact
+__device__ __forceinline__ uint32_t i8_as_f32bits(uint32_t w, int byte) {
+  return __float_as_uint((float)(int8_t)(w >> (8 * byte)));
+}
+// [lo.upper16, hi.upper16] -- two bf16 values from two binary32 bit patterns
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
+// Swap the two groups of a loaded pair into MFMA operand order (see above).
+// Written as inline assembly (the swap rewrites both registers in place, and
+// the builtin's register constraints made the compiler copy loaded registers
+// at the loop head, waiting for loads still in flight).  The compiler does
+// not insert hazard wait states around inline assembly, so the block carries
+// its own: a vector ALU write of a register followed by a permlane read of it
+// needs them.
+__device__ __forceinline__ void pair_to_operands(const uint4& v, uint2& g0, uint2& g1) {
+  uint32_t x = v.x, y = v.y, z = v.z, w = v.w;
+  asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\ts_nop 4"
+               : "+v"(x), "+v"(z), "+v"(y), "+v"(w));
+  g0 = make_uint2(x, y);
+  g1 = make_uint2(z, w);
+}
+
+// K slice s of S (whole rotation blocks of U groups)
+__device__ __forceinline__ void slice_groups(const GemvArgs& a, int s, int& g0, int& g1) {
+  const int nu = a.G / a.U;
+  g0 = (int)((int64_t)s * nu / a.S) * a.U;
+  g1 = (int)((int64_t)(s + 1) * nu / a.S) * a.U;
+}
+
+// fixed-order sum of the wave partials of one round into y (or split partials)
+__device__ __forceinline__ void reduce_round(const GemvArgs& a, const float* part, int NW, int RBR,
+                                             int M, int rb0, int nrb, int round, int s) {
+  const float* pr = part + (round & 1) * NW * RBR * M * kRB;
+  for (int it = threadIdx.x; it < RBR * M * kRB; it += blockDim.x) {
+    const int jr = it / (M * kRB), m = (it / kRB) % M, r = it % kRB;
+    const int j = round * RBR + jr;
+    const int64_t row = (int64_t)(rb0 + j) * kRB + r;
+    if (j < nrb && row < a.N) {
+      float t = 0.f;
+      for (int w = 0; w < NW; ++w) t += pr[((w * RBR + jr) * M + m) * kRB + r];
+      a.out[((int64_t)s * M + m) * a.N + row] = t;
     }
-  };
+  }
+}
 
-  // ---- prologue: x -> x' in LDS.  Each thread owns 16 consecutive elements
-  // of one row of the slice per iteration; an n-block (n <= 1024) is n/16
-  // consecutive lanes of one wave.
-  const int Ks = Cs * CW;
-  const int g16_row = Ks >> 4;
-  const int G16 = M * g16_row;
-  const int iters = (G16 + kThreads - 1) / kThreads;
-  auto load_group = [&](int it, float (&v)[16], uint4& sg) {
-    const int gi = (int)threadIdx.x + it * kThreads;
-    if (gi < G16) {
-      const int m = gi / g16_row;
-      const int64_t k = (int64_t)c0 * CW + (int64_t)(gi - m * g16_row) * 16;
-      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + k);
+// ---------------------------------------------------------------------------
+// PQ2_0
+
+struct Pq2Cfg {
+  static constexpr int GS = 8;    // groups per wave: a 1024-element K-range
+  static constexpr int D = 4;     // row blocks of weight loads in flight
+  static constexpr int RBR = 8;   // row blocks per reduction round
+  static constexpr int MAXW = 8;  // waves per workgroup
+};
+
+// LDS bytes: per wave [GS][M][4 terms][4 kb][32 B] operand bytes, then the
+// partials [2][NW][RBR][M][16] floats
+__host__ __device__ inline int pq2_lds_part_offset(int M, int NW) { return NW * Pq2Cfg::GS * M * 512; }
+__host__ __device__ inline int pq2_lds_bytes(int M, int NW) {
+  return pq2_lds_part_offset(M, NW) + 2 * NW * Pq2Cfg::RBR * M * kRB * 4;
+}
+
+template <int M, bool DALIGN>
+__global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a) {
+  constexpr int GS = Pq2Cfg::GS, D = Pq2Cfg::D, RBR = Pq2Cfg::RBR;
+  constexpr int TILES = (M + 3) / 4;
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int NW = blockDim.x >> 6;
+  const int r16 = lane & 15, kb = lane >> 4;
+
+  int g0, g1;
+  slice_groups(a, blockIdx.y, g0, g1);
+  const int gw = g0 + wave * GS;                // first group of this wave
+  const int vg = min(max(g1 - gw, 0), GS);      // its real groups
+  const int64_t kw0 = (int64_t)gw * 128;        // first element of its K-range
+  uint8_t* areg = lds + wave * (GS * M * 512);  // its operand bytes
+  float* part = reinterpret_cast<float*>(lds + pq2_lds_part_offset(M, NW));
+
+  const int rb0 = (int)((int64_t)blockIdx.x * a.total_rb / a.grid_x);
+  const int rb1 = (int)((int64_t)(blockIdx.x + 1) * a.total_rb / a.grid_x);
+  const int nrb = rb1 - rb0;
+
+  // ---- activation row 0 first (the vector memory counter completes in
+  // order).  Lane l holds positions 16l .. 16l+15 of the wave's K-range: the
+  // codes of one packed word, in group l/8.
+  const bool live = (lane >> 3) < vg;
+  auto load_x = [&](int m, float (&v)[16]) {
+    if (live) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + kw0) + 4 * lane;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 f = src[i];
         v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
       }
-      sg = a.signs ? *reinterpret_cast<const uint4*>(a.signs + k) : make_uint4(0u, 0u, 0u, 0u);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = 0.f;
-      sg = make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  auto stage_group = [&](int it, float (&v)[16], const uint4& sg) {
-    const int gi = (int)threadIdx.x + it * kThreads;
+  float xv0[16];
+  load_x(0, xv0);
+  uint4 sg = make_uint4(0u, 0u, 0u, 0u);
+  if (live && a.signs) sg = *reinterpret_cast<const uint4*>(a.signs + kw0 + 16 * lane);
+
+  // ---- weight loads (pair q: groups 2q, 2q+1 of the wave)
+  uint32_t qoff[GS / 2];
+#pragma unroll
+  for (int q = 0; q < GS / 2; ++q) {
+    const int grp = 2 * q + (kb >> 1);
+    qoff[q] = grp < vg ? (uint32_t)r16 * a.row_bytes + (uint32_t)gw * 32u + 64u * q + 16u * kb : kOutOfRange;
+  }
+  const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)gw * 2u;
+  struct WBuf {
+    uint4 q[GS / 2];
+    uint32_t d[GS / 2];
+  };
+  auto issue = [&](int j, WBuf& b) {
+    const int64_t row0 = (int64_t)(rb0 + j) * kRB;
+    int64_t rows = a.N - row0;
+    rows = rows < 0 ? 0 : (rows > kRB ? kRB : rows);
+    if (j >= nrb) rows = 0;
+    const BufRsrc rq = make_rsrc(a.qs + row0 * a.row_bytes, (uint32_t)rows * a.row_bytes);
+    const BufRsrc rd = make_rsrc(a.dpl + row0 * a.d_row_bytes, (uint32_t)rows * a.d_row_bytes);
+#pragma unroll
+    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q]);
+    if (DALIGN) {
+      const uint4 t = buffer_load_16B(rd, doff);
+      b.d[0] = t.x; b.d[1] = t.y; b.d[2] = t.z; b.d[3] = t.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < GS / 2; ++i)
+        b.d[i] = buffer_load_2B(rd, doff + 4u * i) | (buffer_load_2B(rd, doff + 4u * i + 2u) << 16);
+    }
+  };
+  WBuf wb[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue(i, wb[i]);
+
+  // ---- per-wave prologue: rotation, per-group range scale, e5m2 terms
+  float xr[TILES][GS];   // X * 2^-e of (activation row 4*tile + kb, group)
+  float gsc[TILES][GS];  // 2^-e of that (row, group)
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int g = 0; g < GS; ++g) xr[t][g] = gsc[t][g] = 0.f;
+  {
     const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+    const int pw = lane & 7;                         // packed word in the group
+    const int kb16 = (0x76325410 >> (4 * pw)) & 15;  // {0,1,4,5,2,3,6,7}[pw]
+    uint8_t* dst0 = areg + (lane >> 3) * M * 512 + (kb16 & 3) * 32 + (kb16 >> 2) * 16;
+    // even positions of the word become operand bytes 0..7, odd ones 8..15
+    constexpr int P[16] = {0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;  // int8 sign bit
-      v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (neg << 31));
-    }
+    for (int m = 0; m < M; ++m) {
+      float v[16];
+      if (m == 0) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if (st < a.log2n) {
-        const int h = 1 << st;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if ((i & h) == 0) {
-            const float p = v[i], q = v[i + h];
-            v[i] = p + q;
-            v[i + h] = p - q;
-          }
+        for (int i = 0; i < 16; ++i) v[i] = xv0[i];
+      } else {
+        load_x(m, v);
       }
-    }
 #pragma unroll
-    for (int st = 0; st < 6; ++st) {
-      if (st + 4 < a.log2n) {
-        const int h = 1 << st;
-        const bool upper = (lane & h) != 0;
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;  // int8 sign bit
+        v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (neg << 31));
+      }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __shfl_xor(v[i], h);
-          v[i] = upper ? (p - v[i]) : (v[i] + p);
+      for (int st = 0; st < 4; ++st) {
+        if (st < a.log2n) {
+          const int h = 1 << st;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if ((i & h) == 0) {
+              const float p0 = v[i], p1 = v[i + h];
+              v[i] = p0 + p1;
+              v[i + h] = p0 - p1;
+            }
         }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] *= a.scale;
-    const bool live = gi < G16;
-    const int m = live ? gi / g16_row : 0;
-    const int e0 = live ? (gi - m * g16_row) * 16 : 0;
-    const int c = e0 / CW;
-    uint32_t* dst = xs + (m * MC + c) * CS + (e0 % CW) * F::CHUNK_DW / CW;
-    if (F::FOLD) {
-      // power-of-two range scale of the 128-element group (8 lanes)
+      if (a.log2n > 4) lane_butterfly<1>(v);
+      if (a.log2n > 5) lane_butterfly<2>(v);
+      if (a.log2n > 6) lane_butterfly<4>(v);
+      if (a.log2n > 7) lane_butterfly<8>(v);
+      if (a.log2n > 8) lane_butterfly<16>(v);
+      if (a.log2n > 9) lane_butterfly<32>(v);
+      // range scale of this lane's 128-group (its 8 lanes)
       float mx = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      mx = fmaxf(mx, __shfl_xor(mx, 4));
-      int E = (int)((__float_as_uint(mx) >> 23) & 0xFFu);
-      E = E < 15 ? 15 : (E > 254 ? 254 : E);
-      const float sc = __uint_as_float((uint32_t)(268 - E) << 23);   // 2^(141-E)
-      const float inv = __uint_as_float((uint32_t)(E - 14) << 23);   // 2^(E-141)
-      // fp16 pairs in decode order: (0,2) (1,3) (4,6) (5,7) ...
-      uint32_t h[8];
+      mx = fmaxf(mx, xor_lane<1>(mx));
+      mx = fmaxf(mx, xor_lane<2>(mx));
+      mx = fmaxf(mx, xor_lane<4>(mx));
+      const int e = range_exponent(mx * a.inv_sqrt_n);
+      const float sc = ldexpf(a.inv_sqrt_n, e);
+      float r[16];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const f16x2 pe = {(_Float16)(v[4 * b] * sc), (_Float16)(v[4 * b + 2] * sc)};
-        const f16x2 po = {(_Float16)(v[4 * b + 1] * sc), (_Float16)(v[4 * b + 3] * sc)};
-        h[2 * b] = __builtin_bit_cast(uint32_t, pe);
-        h[2 * b + 1] = __builtin_bit_cast(uint32_t, po);
-      }
-      // X = sum of the staged fp16 values (same dot2 arithmetic as the codes)
-      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-      float part = 0.f;
+      for (int i = 0; i < 16; ++i) r[i] = v[i] = v[i] * sc;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) part = dot2(ones, h[i], part);
-      part += __shfl_xor(part, 1);  // a 64-element chunk is 4 consecutive lanes
-      part += __shfl_xor(part, 2);
-      if (live) {
-        uint4* d4 = reinterpret_cast<uint4*>(dst);
-        d4[0] = make_uint4(h[0], h[1], h[2], h[3]);
-        d4[1] = make_uint4(h[4], h[5], h[6], h[7]);
-        if ((gi & 3) == 0) {
-          xsum[m * MC + c] = part;
-          xinv[m * MC + c] = inv;
+      for (int t = 0; t < 4; ++t) {
+        uint32_t tw[4];
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq) {
+          int w = __builtin_amdgcn_cvt_pk_bf8_f32(r[P[4 * dq]], r[P[4 * dq + 1]], 0, false);
+          w = __builtin_amdgcn_cvt_pk_bf8_f32(r[P[4 * dq + 2]], r[P[4 * dq + 3]], w, true);
+          tw[dq] = (uint32_t)w;
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+          r[P[4 * dq]] -= lo.x;
+          r[P[4 * dq + 1]] -= lo.y;
+          r[P[4 * dq + 2]] -= hi.x;
+          r[P[4 * dq + 3]] -= hi.y;
         }
+        if (live) *reinterpret_cast<uint4*>(dst0 + (m * 4 + t) * 128) = make_uint4(tw[0], tw[1], tw[2], tw[3]);
       }
-    } else if (live) {
-      uint4* d4 = reinterpret_cast<uint4*>(dst);
+      // X = sum of t0 + t1 + t2 + t3 over the group (exact per element)
+      float tsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        d4[i] = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
-                           __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3]));
+      for (int i = 0; i < 16; ++i) tsum += v[i] - r[i];
+      tsum += xor_lane<1>(tsum);
+      tsum += xor_lane<2>(tsum);
+      tsum += xor_lane<4>(tsum);
+      const float inv = ldexpf(1.f, -e);
+      const float xs = tsum * inv;
+      // the lanes whose outputs belong to activation row m take X and 2^-e of
+      // every group from the group's first lane
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const float xg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xs), 8 * g));
+        const float ig = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), 8 * g));
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+          if (4 * t + kb == m && g < vg) {
+            xr[t][g] = xg;
+            gsc[t][g] = ig;
+          }
+      }
+    }
+  }
+  // The operand bytes were written by other lanes of this wave; LDS
+  // instructions of a wave complete in order, so only the compiler must not
+  // move the reads above the writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int aop[TILES][GS][8];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) {
+    const int ma = 4 * t + (r16 >> 2);  // activation row of this lane's operand row
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      if (ma < M && g < vg) {
+        const uint4* p = reinterpret_cast<const uint4*>(areg + ((g * M + ma) * 4 + (r16 & 3)) * 128 + kb * 32);
+        const uint4 p0 = p[0], p1 = p[1];
+        aop[t][g][0] = p0.x; aop[t][g][1] = p0.y; aop[t][g][2] = p0.z; aop[t][g][3] = p0.w;
+        aop[t][g][4] = p1.x; aop[t][g][5] = p1.y; aop[t][g][6] = p1.z; aop[t][g][7] = p1.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) aop[t][g][i] = 0;
+      }
+    }
+  }
+
+  // ---- main loop over row blocks
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const WBuf& b, int j) {
+    uint2 wq[GS];
+#pragma unroll
+    for (int q = 0; q < GS / 2; ++q) pair_to_operands(b.q[q], wq[2 * q], wq[2 * q + 1]);
+    float dg[GS];
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      const float dd = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+      dg[g] = g < vg ? dd : 0.f;
+    }
+    f32x4 Y[TILES];
+    float cr[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      Y[t] = zero;
+      cr[t] = 0.f;
+    }
+    // Two halves of four groups.  The accumulators are read only after a
+    // delay that is tied to them as asm operands: the compiler's wait-state
+    // count for this mixed e5m2 x fp4 MFMA was measured to be too short on
+    // gfx950, and the B registers stay untouched until the delay has passed.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x8 Bq[4];
+      f32x4 acc[TILES][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w0 = wq[4 * h + u].x, w1 = wq[4 * h + u].y;
+        Bq[u] = (i32x8){(int)(w0 & 0x33333333u), (int)((w0 >> 2) & 0x33333333u),
+                        (int)(w1 & 0x33333333u), (int)((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          const int g = 4 * h + u;
+          const i32x8 A = {aop[t][g][0], aop[t][g][1], aop[t][g][2], aop[t][g][3],
+                           aop[t][g][4], aop[t][g][5], aop[t][g][6], aop[t][g][7]};
+          acc[t][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq[u], zero, 1, 4, 0, 127, 0, 127);
+        }
+      static_assert(TILES <= 2, "the delay below lists the accumulators");
+      if constexpr (TILES == 1) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3])
+                     : "v"(Bq[0].lo), "v"(Bq[1].lo), "v"(Bq[2].lo), "v"(Bq[3].lo));
+      } else {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]),
+                       "+v"(acc[TILES - 1][0]), "+v"(acc[TILES - 1][1]), "+v"(acc[TILES - 1][2]),
+                       "+v"(acc[TILES - 1][3])
+                     : "v"(Bq[0].lo), "v"(Bq[1].lo), "v"(Bq[2].lo), "v"(Bq[3].lo));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          const int g = 4 * h + u;
+          const float ds = dg[g] * gsc[t][g];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Y[t][i] = fmaf(ds, acc[t][u][i], Y[t][i]);
+          cr[t] = fmaf(dg[g], xr[t][g], cr[t]);
+        }
+    }
+    float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * kRB;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int mo = 4 * t + kb;
+      if (mo < M) pw[mo * kRB + r16] = 2.f * ((Y[t][0] + Y[t][1]) + (Y[t][2] + Y[t][3])) - cr[t];
     }
   };
 
-  uint4 q0[RB], q1[RB], q2[RB];
-  uint32_t d0[RB], d1[RB], d2[RB];
+  for (int j0 = 0; j0 < nrb; j0 += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int j = j0 + i;
+      if (j < nrb) compute(wb[i], j);
+      issue(j + D, wb[i]);
+      if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
+        __syncthreads();
+        reduce_round(a, part, NW, RBR, M, rb0, nrb, j / RBR, blockIdx.y);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0
+
+struct Q8Cfg {
+  static constexpr int GS = 10;  // groups of 32 per wave
+  static constexpr int D = 2;
+  static constexpr int RBR = 4;
+  static constexpr int MAXW = 16;
+};
+
+// LDS bytes: staged activations f32 [M][NW*GS*32], then the partials
+__host__ __device__ inline int q8_lds_part_offset(int M, int NW) { return M * NW * Q8Cfg::GS * 32 * 4; }
+__host__ __device__ inline int q8_lds_bytes(int M, int NW) {
+  return q8_lds_part_offset(M, NW) + 2 * NW * Q8Cfg::RBR * M * kRB * 4;
+}
+
+// rotation stages with h >= 16 in LDS: butterflies on E = 2^L values at stride 16
+template <int L>
+__device__ void lds_stages_t(float* xs, int KRmax, int KR, int n, int M_) {
+  constexpr int E = 1 << L;
+  const int items = KR / E;
+  for (int m = 0; m < M_; ++m) {
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+      float* p = xs + m * KRmax + (it >> 4) * n + (it & 15);
+      float v[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = p[16 * i];
+#pragma unroll
+      for (int st = 0; st < L; ++st) {
+        const int h = 1 << st;
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+          if ((i & h) == 0) {
+            const float p0 = v[i], p1 = v[i + h];
+            v[i] = p0 + p1;
+            v[i + h] = p0 - p1;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < E; ++i) p[16 * i] = v[i];
+    }
+  }
+}
+__device__ void lds_stages(float* xs, int KRmax, int KR, int log2n, int M_) {
+  const int n = 1 << log2n;
+  switch (log2n) {
+    case 5: lds_stages_t<1>(xs, KRmax, KR, n, M_); break;
+    case 6: lds_stages_t<2>(xs, KRmax, KR, n, M_); break;
+    case 7: lds_stages_t<3>(xs, KRmax, KR, n, M_); break;
+    case 8: lds_stages_t<4>(xs, KRmax, KR, n, M_); break;
+    case 9: lds_stages_t<5>(xs, KRmax, KR, n, M_); break;
+    default: lds_stages_t<6>(xs, KRmax, KR, n, M_); break;
+  }
+}
+
+template <int M, bool DALIGN>
+__global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
+  constexpr int GS = Q8Cfg::GS, D = Q8Cfg::D, RBR = Q8Cfg::RBR;
+  constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NW = blockDim.x >> 6;
+  const int r16 = lane & 15, kb = lane >> 4;
+
+  int g0, g1;
+  slice_groups(a, blockIdx.y, g0, g1);
+  const int KR = (g1 - g0) * 32;
+  const int64_t k0 = (int64_t)g0 * 32;
+  const int gw = wave * GS;  // relative to g0
+  const int vg = min(max(g1 - g0 - gw, 0), GS);
+  const int KRmax = NW * GS * 32;
+  float* xs = reinterpret_cast<float*>(lds);  // [M][KRmax]
+  float* part = reinterpret_cast<float*>(lds + q8_lds_part_offset(M, NW));
+
+  const int rb0 = (int)((int64_t)blockIdx.x * a.total_rb / a.grid_x);
+  const int rb1 = (int)((int64_t)(blockIdx.x + 1) * a.total_rb / a.grid_x);
+  const int nrb = rb1 - rb0;
+
+  // ---- activation loads first (rows past the first four after the weight
+  // loads, to bound the registers held)
+  constexpr int MPRE = M < 4 ? M : 4;
+  const int U16 = KR >> 4;  // 16-element units per activation row (<= threads)
+  const bool has_unit = tid < U16;
+  auto load_row = [&](int m, float (&v)[16]) {
+    if (has_unit) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + k0) + 4 * tid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = src[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.f;
+    }
+  };
+  float xv[MPRE][16];
+  uint4 sg = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int m = 0; m < MPRE; ++m) load_row(m, xv[m]);
+  if (has_unit && a.signs) sg = *reinterpret_cast<const uint4*>(a.signs + k0 + 16 * tid);
+
+  // ---- weight loads (pair q: groups 2q, 2q+1 of the wave)
+  uint32_t qoff[GS / 2];
+#pragma unroll
+  for (int q = 0; q < GS / 2; ++q) {
+    const int grp = 2 * q + (kb >> 1);
+    qoff[q] = grp < vg ? (uint32_t)r16 * a.row_bytes + (uint32_t)(g0 + gw) * 32u + 64u * q + 16u * kb
+                       : kOutOfRange;
+  }
+  const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)(g0 + gw) * 2u;
+  struct WBuf {
+    uint4 q[GS / 2];
+    uint32_t d[DW];
+  };
+  auto issue = [&](int j, WBuf& b) {
+    const int64_t row0 = (int64_t)(rb0 + j) * kRB;
+    int64_t rows = a.N - row0;
+    rows = rows < 0 ? 0 : (rows > kRB ? kRB : rows);
+    if (j >= nrb) rows = 0;
+    const BufRsrc rq = make_rsrc(a.qs + row0 * a.row_bytes, (uint32_t)rows * a.row_bytes);
+    const BufRsrc rd = make_rsrc(a.dpl + row0 * a.d_row_bytes, (uint32_t)rows * a.d_row_bytes);
+#pragma unroll
+    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q]);
+    if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
+#pragma unroll
+      for (int i = 0; i < DW / 4; ++i) {
+        const uint4 t = buffer_load_16B(rd, doff + 16u * i);
+        b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
+      }
+      if (DW % 4 >= 2) {
+        const uint2 t = buffer_load_8B(rd, doff + 16u * (DW / 4));
+        b.d[DW / 4 * 4] = t.x; b.d[DW / 4 * 4 + 1] = t.y;
+      }
+      if (DW % 2)
+        b.d[DW - 1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(doff + 4u * (DW - 1)), 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DW; ++i) {
+        const uint32_t lo = buffer_load_2B(rd, doff + 4u * i);
+        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, doff + 4u * i + 2u) : 0u;
+        b.d[i] = lo | (hi << 16);
+      }
+    }
+  };
+  WBuf wb[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue(i, wb[i]);
+
+  // ---- prologue: stage x (.) s in LDS, butterflies with stride < 16 in
+  // registers, wider ones in LDS
   {
-    float v[16];
-    uint4 sg;
-    // activation loads first, then the first two weight steps, so that the
-    // prologue only waits for the (small) activation loads
-    // waves with no element in an iteration skip it (uniform; the shuffles
-    // never leave a wave)
-    const int wave_first = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
-    load_group(0, v, sg);
-    if (n_steps > 0) load_step(0, q0, d0);
-    if (n_steps > 1) load_step(1, q1, d1);
-    if (wave_first < G16) stage_group(0, v, sg);
-    for (int it = 1; it < iters; ++it) {
-      load_group(it, v, sg);
-      if (wave_first + it * kThreads < G16) stage_group(it, v, sg);
+    const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v[16];
+      if (m < MPRE) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = xv[m < MPRE ? m : 0][i];
+      } else {
+        load_row(m, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;  // int8 sign bit
+        v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (neg << 31));
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st < a.log2n) {
+          const int h = 1 << st;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if ((i & h) == 0) {
+              const float p0 = v[i], p1 = v[i + h];
+              v[i] = p0 + p1;
+              v[i + h] = p0 - p1;
+            }
+        }
+      }
+      if (has_unit) {
+        float4* dst = reinterpret_cast<float4*>(xs + m * KRmax) + 4 * tid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      }
     }
   }
   __syncthreads();
+  if (a.log2n > 4) {
+    lds_stages(xs, KRmax, KR, a.log2n, M);
+    __syncthreads();
+  }
 
-  float acc[RB][M], tacc[RB][M];
+  // ---- operand: lane (i, kb) holds activation row i/2 (hi part for even i,
+  // lo for odd i) at the 8 positions that operand block kb covers
+  int aop[GS][4];
+  {
+    const int ma = r16 >> 1;
+    const bool lo_part = r16 & 1;
+    const int base = ((kb & 1) << 4) | ((kb & 2) << 2);  // {0, 16, 8, 24}[kb]
 #pragma unroll
-  for (int j = 0; j < RB; ++j)
+    for (int g = 0; g < GS; ++g) {
+      if (ma < M && g < vg) {
+        const float4* p = reinterpret_cast<const float4*>(xs + ma * KRmax + (gw + g) * 32 + base);
+        const float4 f0 = p[0], f1 = p[1];
+        const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[j][m] = tacc[j][m] = 0.f;
-
-  auto body = [&](int step, uint4 (&cq)[RB], uint32_t (&cd)[RB], uint4 (&pq)[RB], uint32_t (&pd)[RB]) {
-    if (step >= n_steps) return;
-    if (step + 2 < n_steps) load_step(step + 2, pq, pd);
-    const int b = step / steps_per_batch;
-    const int p = step - b * steps_per_batch;
-    const bool tail = p == Qs;
-    const int64_t row0 = r_begin + (int64_t)b * RB;
-    const int rows_here = (int)(r_end - row0 < RB ? r_end - row0 : RB);
-    const int chunk = tail ? tail_chunk : (p << 6) + lane;
-    // rows with data in this step (uniform); idle tail lanes hold zero codes
-    // and zero scales, so they add nothing
-    const int nloads = __builtin_amdgcn_readfirstlane(tail ? RBt : rows_here);
-
-    float S[RB][M];
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
-#pragma unroll
-      for (int m = 0; m < M; ++m) S[j][m] = 0.f;
-#pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-      uint32_t xw[M][F::XDW];
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const uint4* src = reinterpret_cast<const uint4*>(xs + (m * MC + chunk) * CS + wi * F::XDW);
-#pragma unroll
-        for (int i = 0; i < F::XDW / 4; ++i) {
-          const uint4 t = src[i];
-          xw[m][4 * i] = t.x; xw[m][4 * i + 1] = t.y; xw[m][4 * i + 2] = t.z; xw[m][4 * i + 3] = t.w;
+        for (int i = 0; i < 4; ++i) {
+          const float e0 = v[2 * i] * a.inv_sqrt_n, e1 = v[2 * i + 1] * a.inv_sqrt_n;
+          const uint32_t hh = pack_bf16x2(e0, e1);
+          const uint32_t ll = pack_bf16x2(e0 - bf16_bits_to_f32(hh & 0xFFFFu), e1 - bf16_bits_to_f32(hh >> 16));
+          aop[g][i] = (int)(lo_part ? ll : hh);
         }
-      }
+      } else {
 #pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        if (j < nloads) {
-          const uint32_t w = wi == 0 ? cq[j].x : wi == 1 ? cq[j].y : wi == 2 ? cq[j].z : cq[j].w;
-          if (FMT == kFmtPQ2) {
-            const uint32_t e = w & 0x33333333u;         // codes 0,2,..,14 (one per nibble)
-            const uint32_t o = (w >> 2) & 0x33333333u;  // codes 1,3,..,15
-            f16x2 h[8];
-            h[0] = codes2h<0>(e); h[1] = codes2h<0>(o);
-            h[2] = codes2h<1>(e); h[3] = codes2h<1>(o);
-            h[4] = codes2h<2>(e); h[5] = codes2h<2>(o);
-            h[6] = codes2h<3>(e); h[7] = codes2h<3>(o);
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-              for (int i = 0; i < 8; ++i) S[j][m] = dot2(h[i], xw[m][i], S[j][m]);
-          } else {
-            float v[4];
-            v[0] = (float)(int8_t)(w);
-            v[1] = (float)(int8_t)(w >> 8);
-            v[2] = (float)(int8_t)(w >> 16);
-            v[3] = (float)(int8_t)(w >> 24);
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) S[j][m] = fmaf(v[i], __uint_as_float(xw[m][i]), S[j][m]);
-          }
-        }
+        for (int i = 0; i < 4; ++i) aop[g][i] = 0;
       }
     }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float X = F::FOLD ? xsum[m * MC + chunk] : 0.f;
-      const float inv = F::FOLD ? xinv[m * MC + chunk] : 1.f;
-#pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        if (j < nloads) {
-          const float t = F::FOLD ? (S[j][m] - X) : S[j][m];
-          const float dj = F::FOLD ? f16_bits_to_f32(cd[j]) * inv : f16_bits_to_f32(cd[j]);
-          if (tail)
-            tacc[j][m] = fmaf(dj, t, tacc[j][m]);
-          else
-            acc[j][m] = fmaf(dj, t, acc[j][m]);
-        }
-      }
-    }
+  }
 
-    // ---- end of a batch: reduce and store
-    if (p == steps_per_batch - 1) {
-      float mine[M];
+  // ---- main loop over row blocks
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const WBuf& b, int j) {
+    f32x4 Y = zero;
 #pragma unroll
-      for (int m = 0; m < M; ++m) mine[m] = 0.f;
+    for (int q = 0; q < GS / 2; ++q) {
+      uint2 wq[2];
+      pair_to_operands(b.q[q], wq[0], wq[1]);
 #pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        if (j < rows_here) {
+      for (int h = 0; h < 2; ++h) {
+        const int g = 2 * q + h;
+        const float dd = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+        const float dg = g < vg ? dd : 0.f;
+        const uint32_t w0 = wq[h].x, w1 = wq[h].y;
+        const uint4 bq = make_uint4(bf16_pair(i8_as_f32bits(w0, 0), i8_as_f32bits(w0, 1)),
+                                    bf16_pair(i8_as_f32bits(w0, 2), i8_as_f32bits(w0, 3)),
+                                    bf16_pair(i8_as_f32bits(w1, 0), i8_as_f32bits(w1, 1)),
+                                    bf16_pair(i8_as_f32bits(w1, 2), i8_as_f32bits(w1, 3)));
+        const uint4 aq = make_uint4((uint32_t)aop[g][0], (uint32_t)aop[g][1], (uint32_t)aop[g][2],
+                                    (uint32_t)aop[g][3]);
+        const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, aq), __builtin_bit_cast(bf16x8, bq), zero, 0, 0, 0);
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const float tot = wave_sum(acc[j][m]);
-            mine[m] = lane == j ? tot : mine[m];
-          }
-        }
+        for (int i = 0; i < 4; ++i) Y[i] = fmaf(dg, acc[i], Y[i]);
       }
-      if (Ts >= 2 && (Ts & (Ts - 1)) == 0 && Ts <= 32) {
-        // tail partials: lane l of tail load j holds row G*j + l/Ts; sum each
-        // aligned group of Ts lanes with DPP, then read the group totals
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          if (j < RBt) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              const float t = group_sum_pow2(tacc[j][m], Ts);
-              for (int g = 0; g < G; ++g) {
-                const int r = G * j + g;
-                const float tr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), g * Ts));
-                if (r < rows_here) mine[m] = lane == r ? mine[m] + tr : mine[m];
-              }
-            }
-          }
-        }
-      } else if (Ts) {
-        // other tails: through the per-wave LDS scratch (LDS operations of a
-        // wave complete in order; only compiler reordering must be stopped)
-#pragma unroll
-        for (int j = 0; j < RB; ++j)
-#pragma unroll
-          for (int m = 0; m < M; ++m) scratch[(j * M + m) * 64 + lane] = tacc[j][m];
-        __builtin_amdgcn_wave_barrier();
-        if (lane < rows_here) {
-          const int jt = lane / G, gt = lane - jt * G;
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const float* src = scratch + (jt * M + m) * 64 + gt * Ts;
-            float t = 0.f;
-            for (int i = 0; i < Ts; ++i) t += src[i];
-            mine[m] += t;
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-      if (lane < rows_here) {
-        float* o = a.out + (int64_t)s * M * a.N + row0 + lane;
-#pragma unroll
-        for (int m = 0; m < M; ++m) o[(int64_t)m * a.N] = mine[m];
-      }
-#pragma unroll
-      for (int j = 0; j < RB; ++j)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[j][m] = tacc[j][m] = 0.f;
     }
+    float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * kRB;
+    const int m0 = 2 * kb;
+    if (m0 < M) pw[m0 * kRB + r16] = Y[0] + Y[1];
+    if (m0 + 1 < M) pw[(m0 + 1) * kRB + r16] = Y[2] + Y[3];
   };
 
-  // three rotating register buffers: step s computes from buffer s % 3 and
-  // prefetches step s + 2 into buffer (s + 2) % 3
-  for (int step = 0; step < n_steps; step += 3) {
-    body(step, q0, d0, q2, d2);
-    body(step + 1, q1, d1, q0, d0);
-    body(step + 2, q2, d2, q1, d1);
+  for (int j0 = 0; j0 < nrb; j0 += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int j = j0 + i;
+      if (j < nrb) compute(wb[i], j);
+      issue(j + D, wb[i]);
+      if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
+        __syncthreads();
+        reduce_round(a, part, NW, RBR, M, rb0, nrb, j / RBR, blockIdx.y);
+      }
+    }
   }
 }
 
@@ -483,139 +762,120 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   y[i] = t;
 }
 
-static int rows_per_batch(int64_t M) { return M <= 2 ? 8 : (M <= 4 ? 4 : 2); }
-static constexpr int kLdsBudget = 120 * 1024;
-static constexpr int kTargetWaves = 2048;  // 256 CUs x 4 SIMDs x 2
+// ---------------------------------------------------------------------------
+// host side
 
-// LDS per workgroup: staged x' (+ per-chunk sum and range scale for PQ2_0)
-// and, only when some K-slice has a tail step, the per-wave tail scratch.
-static int64_t lds_bytes_for(int fmt, int64_t M, int n_groups, int S) {
-  const int chunk_dw = fmt == kFmtPQ2 ? 32 : 16;
-  const int chunks = 2 * ((n_groups + S - 1) / S);
-  int64_t b = M * chunks * (chunk_dw + kPadDW) * 4;
-  if (fmt == kFmtPQ2) b += 2 * M * chunks * 4;
-  bool tail = false;
-  for (int s = 0; s < S; ++s) {
-    const int g0 = (int)((int64_t)s * n_groups / S), g1 = (int)((int64_t)(s + 1) * n_groups / S);
-    tail = tail || ((2 * (g1 - g0)) & 63) != 0;
-  }
-  if (tail) b += (int64_t)kWaves * rows_per_batch(M) * M * 64 * 4;  // (used for odd tails only)
-  return b;
-}
-
-GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int split_req) {
+GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req) {
   GemvPlan p{};
-  const int n_groups = (int)(K / group_of(fmt));
-  int s_min = 1;
-  while (s_min <= n_groups && lds_bytes_for(fmt, M, n_groups, s_min) > kLdsBudget) ++s_min;
-  int S = split_req > 0 ? split_req : s_min;
-  if (S > n_groups || S < 1 || lds_bytes_for(fmt, M, n_groups, S) > kLdsBudget) {
-    p.split = -1;
-    return p;
+  p.split = -1;
+  const bool pq2 = fmt == kFmtPQ2;
+  const int GROUP = pq2 ? 128 : 32;
+  const int GS = pq2 ? Pq2Cfg::GS : Q8Cfg::GS;
+  const int MAXW = pq2 ? Pq2Cfg::MAXW : Q8Cfg::MAXW;
+  const int G = (int)(K / GROUP);
+  const int n = block_len > 1 ? block_len : 1;
+  const int U = n > GROUP ? n / GROUP : 1;
+  const int NU = G / U;
+  auto waves_for = [&](int S) {
+    const int gmax = (NU + S - 1) / S * U;
+    return (gmax + GS - 1) / GS;
+  };
+  auto lds_for = [&](int S) {
+    const int nw = waves_for(S);
+    return pq2 ? pq2_lds_bytes((int)M, nw) : q8_lds_bytes((int)M, nw);
+  };
+  auto fits = [&](int S) { return waves_for(S) <= MAXW && lds_for(S) <= kLdsBudget; };
+  int S;
+  if (split_req > 0) {
+    S = split_req;
+    if (S > NU || !fits(S)) return p;
+  } else {
+    S = 1;
+    while (S <= NU && !fits(S)) ++S;
+    if (S > NU) return p;
   }
   p.split = S;
-  p.lds_bytes = (int)lds_bytes_for(fmt, M, n_groups, S);
-  int64_t waves = kTargetWaves / S;
-  if (waves < kWaves) waves = kWaves;
-  int64_t rpw = (N + waves - 1) / waves;
-  if (rpw < 1) rpw = 1;
-  p.rows_per_wave = (int)rpw;
-  int64_t w_needed = (N + rpw - 1) / rpw;
-  p.grid_x = (int)((w_needed + kWaves - 1) / kWaves);
+  p.units = U;
+  p.nw = waves_for(S);
+  p.lds_bytes = lds_for(S);
+  p.total_rb = (int)((N + kRB - 1) / kRB);
+  const int target = kTargetWGs / S > 0 ? kTargetWGs / S : 1;
+  p.grid_x = p.total_rb < target ? p.total_rb : target;
+  // scale runs of a wave start on a 4-byte boundary when every slice starts
+  // on an even group and rows hold an even number of groups
+  bool even = G % 2 == 0;
+  for (int s = 0; s < S && even; ++s) even = ((int64_t)s * NU / S * U) % 2 == 0;
+  p.dalign = even;
   return p;
-}
-
-// The rotation runs inside the GEMV prologue when every K-slice starts on an
-// n-block boundary; otherwise a separate pre-pass writes x' to the workspace.
-static bool rotation_fused(int fmt, int n_groups, int S, int block_len) {
-  if (block_len <= 1) return true;
-  const int g = group_of(fmt);
-  for (int s = 0; s < S; ++s) {
-    const int64_t k0 = (int64_t)s * n_groups / S * g;
-    if (k0 % block_len) return false;
-  }
-  return (int64_t)n_groups * g % block_len == 0;
 }
 
 int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int block_len,
                              int split_req) {
-  GemvPlan p = plan_gemv(fmt, M, N, K, split_req);
+  GemvPlan p = plan_gemv(fmt, M, N, K, block_len, split_req);
   if (p.split < 1) return -1;
-  const int n_groups = (int)(K / group_of(fmt));
-  int64_t b = 0;
-  if (!rotation_fused(fmt, n_groups, p.split, block_len)) b += (M * K * 4 + 255) / 256 * 256;
-  if (p.split > 1) b += (int64_t)p.split * M * N * 4;
-  return b;
+  return p.split > 1 ? (int64_t)p.split * M * N * 4 : 0;
 }
 
-template <int FMT, int M>
-static int launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
-  // more than 64 KiB of dynamic LDS needs the attribute; set once per
-  // instantiation (thread-safe static initialisation)
-  static const bool attr_ok =
-      hipFuncSetAttribute((const void*)gemv_kernel<FMT, M>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) == hipSuccess;
-  if (!attr_ok) return -1;
-  dim3 grid(p.grid_x, p.split);
-  gemv_kernel<FMT, M><<<grid, kThreads, p.lds_bytes, st>>>(a);
+template <typename Kernel>
+static int launch_kernel(Kernel k, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  // more than 64 KiB of dynamic LDS needs the attribute
+  if (p.lds_bytes > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+          hipSuccess)
+    return -1;
+  hipLaunchKernelGGL(k, dim3(p.grid_x, p.split), dim3(p.nw * 64), p.lds_bytes, st, a);
   return 0;
 }
 
-template <int FMT>
-static int launch_fmt(int64_t M, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
-  switch (M) {
-    case 1: return launch_one<FMT, 1>(a, p, st);
-    case 2: return launch_one<FMT, 2>(a, p, st);
-    case 3: return launch_one<FMT, 3>(a, p, st);
-    case 4: return launch_one<FMT, 4>(a, p, st);
-    case 5: return launch_one<FMT, 5>(a, p, st);
-    case 6: return launch_one<FMT, 6>(a, p, st);
-    case 7: return launch_one<FMT, 7>(a, p, st);
-    default: return launch_one<FMT, 8>(a, p, st);
-  }
+template <int M>
+static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  if (fmt == kFmtPQ2)
+    return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true>, a, p, st)
+                    : launch_kernel(gemv_pq2_kernel<M, false>, a, p, st);
+  return p.dalign ? launch_kernel(gemv_q8_kernel<M, true>, a, p, st)
+                  : launch_kernel(gemv_q8_kernel<M, false>, a, p, st);
 }
 
 int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,
                 int block_len, const int8_t* signs, int split_req, float* y, void* ws,
                 hipStream_t st) {
-  GemvPlan p = plan_gemv(fmt, M, N, K, split_req);
+  GemvPlan p = plan_gemv(fmt, M, N, K, block_len, split_req);
   if (p.split < 1) return -2;
-  const int n_groups = (int)(K / group_of(fmt));
-  GemvArgs a;
-  uint8_t* wsp = (uint8_t*)ws;
-  if (rotation_fused(fmt, n_groups, p.split, block_len)) {
-    a.x = x;
-    a.signs = signs;
-    int log2n = 0;
-    while ((1 << log2n) < block_len) ++log2n;
-    a.log2n = log2n;
-    a.scale = block_len > 1 ? (float)(1.0 / __builtin_sqrt((double)block_len)) : 1.0f;
-  } else {
-    float* xprime = (float*)wsp;
-    if (launch_hadamard(x, 0, xprime, 0, M, K, block_len, signs, st)) return -1;
-    wsp += (M * K * 4 + 255) / 256 * 256;
-    a.x = xprime;
-    a.signs = nullptr;
-    a.log2n = 0;
-    a.scale = 1.0f;
-  }
   PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
+  GemvArgs a;
   a.qs = pv.qs;
-  a.dpl = (const uint16_t*)pv.d;
+  a.dpl = pv.d;
+  a.x = x;
+  a.signs = signs;
   a.N = N;
   a.K = K;
-  a.row_bytes = (int)pv.row_bytes;
-  a.d_per_row = (int)pv.d_per_row;
-  a.n_groups = n_groups;
-  a.split = p.split;
-  a.rows_per_wave = p.rows_per_wave;
-  a.max_slice_chunks = 2 * ((n_groups + p.split - 1) / p.split);
-  float* part = p.split > 1 ? (float*)wsp : nullptr;
+  a.row_bytes = (uint32_t)pv.row_bytes;
+  a.d_row_bytes = (uint32_t)(pv.d_per_row * 2);
+  a.G = (int)(K / (fmt == kFmtPQ2 ? 128 : 32));
+  a.U = p.units;
+  a.S = p.split;
+  a.total_rb = p.total_rb;
+  a.grid_x = p.grid_x;
+  int log2n = 0;
+  while (block_len > 1 && (1 << log2n) < block_len) ++log2n;
+  a.log2n = log2n;
+  a.inv_sqrt_n = block_len > 1 ? (float)(1.0 / __builtin_sqrt((double)block_len)) : 1.0f;
+  float* part = p.split > 1 ? (float*)ws : nullptr;
   a.out = p.split > 1 ? part : y;
-  const int rc = fmt == kFmtPQ2 ? launch_fmt<kFmtPQ2>(M, a, p, st) : launch_fmt<kFmtQ8>(M, a, p, st);
+  int rc;
+  switch (M) {
+    case 1: rc = launch_m<1>(fmt, a, p, st); break;
+    case 2: rc = launch_m<2>(fmt, a, p, st); break;
+    case 3: rc = launch_m<3>(fmt, a, p, st); break;
+    case 4: rc = launch_m<4>(fmt, a, p, st); break;
+    case 5: rc = launch_m<5>(fmt, a, p, st); break;
+    case 6: rc = launch_m<6>(fmt, a, p, st); break;
+    case 7: rc = launch_m<7>(fmt, a, p, st); break;
+    default: rc = launch_m<8>(fmt, a, p, st); break;
+  }
   if (rc || hipGetLastError() != hipSuccess) return -1;
   if (p.split > 1) {
-    int64_t n = M * N;
+    const int64_t n = M * N;
     splitk_reduce_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(part, y, n, p.split);
     if (hipGetLastError() != hipSuccess) return -1;
   }

@@ -39,14 +39,17 @@ int launch_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W, h
 int launch_hadamard(const void* x, int x_bf16, void* xr, int xr_bf16, int64_t M, int64_t K,
                     int n, const int8_t* signs, hipStream_t st);
 
-// GEMV plan: how K is split and how rows map to waves.
+// GEMV plan: how K is split across workgroups and how the grid is shaped.
 struct GemvPlan {
-  int split;          // S >= 1 K-ranges
-  int rows_per_wave;  // contiguous rows owned by one wave
-  int grid_x;         // workgroups along the rows
-  int lds_bytes;      // dynamic LDS per workgroup
+  int split;      // S >= 1 K-slices (grid.y); < 1 if no plan fits
+  int units;      // groups per rotation block (slices hold whole blocks)
+  int nw;         // waves per workgroup
+  int grid_x;     // workgroups along the rows
+  int total_rb;   // 16-row blocks
+  int lds_bytes;  // dynamic LDS per workgroup
+  bool dalign;    // per-wave scale runs start on a 4-byte boundary
 };
-GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int split_req);
+GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req);
 int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req);
 int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,
                 int block_len, const int8_t* signs, int split_req, float* y, void* ws,

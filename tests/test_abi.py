@@ -56,8 +56,11 @@ def test_workspace_sizes():
     assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 128, 0) == 0
     # split-K: S*M*N fp32 partials
     assert kq.kq_workspace_bytes(0, 1, 1, 248320, 5120, 128, 2) == 2 * 248320 * 4
-    # n = 1024 blocks cut by a K-slice boundary (13 * 128): x' pre-pass + partials
-    assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 1024, 3) == 20480 + 3 * 10240 * 4
+    # K-slices hold whole rotation blocks (n = 1024: 5 blocks over 3 slices):
+    # still only the partials
+    assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 1024, 3) == 3 * 10240 * 4
+    # more slices than rotation blocks: no plan
+    assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 1024, 6) == 0
     assert kq.kq_workspace_bytes(1, 1, 2048, 10240, 5120, 128, 0) == 2048 * 5120 * 2
     assert kq.kq_workspace_bytes(0, 1, 9, 64, 128, 0, 0) == 0   # M > 8
     assert kq.kq_workspace_bytes(0, 1, 1, 64, 100, 0, 0) == 0   # bad K
@@ -133,10 +136,12 @@ def test_gemv_rejections():
     assert need == 2 * 64 * 4                  # S*M*N*4 partials
     assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 0, None, 2, FAKE, None, 0, 0) == "KQ_EWORKSPACE"
     assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 0, None, 2, FAKE, FAKE, need - 4, 0) == "KQ_EWORKSPACE"
-    # a 1024-block cut by a slice boundary needs the x' pre-pass buffer too
+    # slices hold whole rotation blocks: 1024-blocks over 3 slices need only
+    # the partials; more slices than blocks is a valid request with no plan
     need = kq.kq_workspace_bytes(0, 1, 1, 64, 5120, 1024, 3)
-    assert need == 5120 * 4 + 3 * 64 * 4
-    assert _status(g, 1, FAKE, 64, 5120, FAKE, 1, 1024, None, 3, FAKE, FAKE, 3 * 64 * 4, 0) == "KQ_EWORKSPACE"
+    assert need == 3 * 64 * 4
+    assert _status(g, 1, FAKE, 64, 5120, FAKE, 1, 1024, None, 3, FAKE, FAKE, need - 4, 0) == "KQ_EWORKSPACE"
+    assert _status(g, 1, FAKE, 64, 5120, FAKE, 1, 1024, None, 6, FAKE, FAKE, ws, 0) == "KQ_EUNSUPPORTED"
 
 
 @pytest.mark.usefixtures("nogpu")
