@@ -217,13 +217,7 @@ def main():
     t_h, _ = time_graph(had_only * len(steps), max(1, replays // 4), 2, stream)
     t_had = t_h / len(steps)
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "gemv_pq2_k5120_n10240_traffic.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            tj = json.load(f)
-        if tj.get("kernel_source_sha") == kernel_source_sha():
-            traffic = tj.get("bytes_per_launch")
+    traffic = measured_traffic()
 
     value = gbs(weight_bytes, t_step)
     result = {
@@ -260,6 +254,24 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W_host, x_host, N, K, n, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed PMC summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy), or None when the GEMV source has
+    changed since the counters were taken."""
+    tfile = os.path.join(ROOT, "profiles", "gemv_pq2_k5120_n10240_traffic.txt")
+    if not os.path.exists(tfile):
+        return None
+    fields = {}
+    with open(tfile) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return int(fields["bytes_per_launch"])
 
 
 def kernel_source_sha():
