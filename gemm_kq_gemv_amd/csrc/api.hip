@@ -107,7 +107,7 @@ kq_status kq_gemv(kq_format fmt, const void* packed, int64_t N, int64_t K, const
       (workspace && !aligned16(workspace)))
     return KQ_EALIGN;
   kq::GemvPlan plan = kq::plan_gemv(fmt, M, N, K, block_len, split_k);
-  if (plan.split < 1) return KQ_EUNSUPPORTED;  // no K split of this size fits the LDS budget
+  if (plan.split < 1) return KQ_EUNSUPPORTED;  // no split fits the LDS or buffer-range limits
   const int64_t need = kq::gemv_workspace_bytes(fmt, M, N, K, block_len, split_k);
   if (need > 0 && (!workspace || (int64_t)ws_bytes < need)) return KQ_EWORKSPACE;
   const int rc = kq::launch_gemv(fmt, packed, N, K, x, M, block_len, signs, split_k, y, workspace,

@@ -55,6 +55,13 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRB = 16;  // weight rows per block (MFMA width)
+// Weight loads go through one buffer resource per plane and workgroup, based
+// at its first row and at most kMaxWgBytes long.  Row blocks past the
+// workgroup's range are loaded at kFarRows, outside that range, so they
+// return zeros without touching memory; every offset stays below 2^31 + 2^30,
+// clear of wrap-around in the range check.
+constexpr uint32_t kFarRows = 0x40000000u;
+constexpr int64_t kMaxWgBytes = int64_t(1) << 29;
 constexpr int kLdsBudget = 160 * 1024;
 constexpr int kTargetWGs = 256;  // one workgroup per CU
 
@@ -72,6 +79,8 @@ struct GemvArgs {
   int S;                 // K slices
   int total_rb;          // 16-row blocks
   int grid_x;
+  int rb_base, rb_rem;   // workgroup b owns row blocks [b*rb_base + min(b, rb_rem), next)
+  int u_base, u_rem;     // slice s owns rotation blocks [s*u_base + min(s, u_rem), next)
   int log2n;             // rotation block length (0: no transform)
   float inv_sqrt_n;
 };
@@ -114,11 +123,11 @@ __device__ __forceinline__ float xor_lane(float v) {
 
 // butterfly across lanes at distance DIST: the lower lane keeps a + b, the
 // upper one a - b (natural-order Sylvester stage)
-template <int DIST>
-__device__ __forceinline__ void lane_butterfly(float (&v)[16]) {
+template <int DIST, int NV>
+__device__ __forceinline__ void lane_butterfly(float (&v)[NV]) {
   const float sgn = (threadIdx.x & DIST) ? -1.f : 1.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = fmaf(sgn, v[i], xor_lane<DIST>(v[i]));
+  for (int i = 0; i < NV; ++i) v[i] = fmaf(sgn, v[i], xor_lane<DIST>(v[i]));
 }
 
 // power-of-two exponent e that puts bound * 2^e in [2^14, 2^15)
@@ -152,11 +161,14 @@ __device__ __forceinline__ void pair_to_operands(const uint4& v, uint2& g0, uint
   g1 = make_uint2(z, w);
 }
 
+// start of part i when parts of `base` items get one more for i < rem
+__host__ __device__ __forceinline__ int part_start(int i, int base, int rem) {
+  return i * base + (i < rem ? i : rem);
+}
 // K slice s of S (whole rotation blocks of U groups)
 __device__ __forceinline__ void slice_groups(const GemvArgs& a, int s, int& g0, int& g1) {
-  const int nu = a.G / a.U;
-  g0 = (int)((int64_t)s * nu / a.S) * a.U;
-  g1 = (int)((int64_t)(s + 1) * nu / a.S) * a.U;
+  g0 = part_start(s, a.u_base, a.u_rem) * a.U;
+  g1 = part_start(s + 1, a.u_base, a.u_rem) * a.U;
 }
 
 // fixed-order sum of the wave partials of one round into y (or split partials)
@@ -178,24 +190,61 @@ __device__ __forceinline__ void reduce_round(const GemvArgs& a, const float* par
 // ---------------------------------------------------------------------------
 // PQ2_0
 
+// EPL activation elements per lane in the prologue: 8 (half a packed code
+// word per lane, GS = 4 groups per wave) for rotation blocks up to 512, 16 (a
+// whole word, GS = 8) for 1024-blocks, which must sit inside one wave.
+template <int EPL>
 struct Pq2Cfg {
-  static constexpr int GS = 8;    // groups per wave: a 1024-element K-range
-  static constexpr int D = 4;     // row blocks of weight loads in flight
-  static constexpr int RBR = 8;   // row blocks per reduction round
-  static constexpr int MAXW = 8;  // waves per workgroup
+  static constexpr int LOG_EPL = EPL == 8 ? 3 : 4;
+  static constexpr int GS = EPL / 2;     // groups per wave: 64 lanes x EPL elements
+  static constexpr int LPG = 128 / EPL;  // lanes per 128-group
+  static constexpr int LPW = 16 / EPL;   // lanes per packed code word
+  static constexpr int D = 4;            // row blocks of weight loads in flight
+  static constexpr int RBR = 8;          // row blocks per reduction round
+  static constexpr int MAXW = EPL == 8 ? 12 : 8;  // 12: up to 168 VGPRs per lane
 };
 
 // LDS bytes: per wave [GS][M][4 terms][4 kb][32 B] operand bytes, then the
 // partials [2][NW][RBR][M][16] floats
-__host__ __device__ inline int pq2_lds_part_offset(int M, int NW) { return NW * Pq2Cfg::GS * M * 512; }
-__host__ __device__ inline int pq2_lds_bytes(int M, int NW) {
-  return pq2_lds_part_offset(M, NW) + 2 * NW * Pq2Cfg::RBR * M * kRB * 4;
+__host__ __device__ inline int pq2_lds_part_offset(int M, int NW, int GS) { return NW * GS * M * 512; }
+__host__ __device__ inline int pq2_lds_bytes(int M, int NW, int GS) {
+  return pq2_lds_part_offset(M, NW, GS) + 2 * NW * 8 * M * kRB * 4;
 }
 
-template <int M, bool DALIGN>
-__global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a) {
-  constexpr int GS = Pq2Cfg::GS, D = Pq2Cfg::D, RBR = Pq2Cfg::RBR;
+// butterflies of the element bits above the in-lane ones (lane distance 1..32)
+template <int LOG_EPL, int NV>
+__device__ __forceinline__ void cross_lane_stages(float (&v)[NV], int log2n) {
+  if (log2n > LOG_EPL) lane_butterfly<1>(v);
+  if (log2n > LOG_EPL + 1) lane_butterfly<2>(v);
+  if (log2n > LOG_EPL + 2) lane_butterfly<4>(v);
+  if (log2n > LOG_EPL + 3) lane_butterfly<8>(v);
+  if (log2n > LOG_EPL + 4) lane_butterfly<16>(v);
+  if (log2n > LOG_EPL + 5) lane_butterfly<32>(v);
+}
+// max / sum over the LPG lanes of one 128-group
+template <int LPG>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, xor_lane<1>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  if constexpr (LPG == 16) v = fmaxf(v, xor_lane<8>(v));
+  return v;
+}
+template <int LPG>
+__device__ __forceinline__ float group_sum(float v) {
+  v += xor_lane<1>(v);
+  v += xor_lane<2>(v);
+  v += xor_lane<4>(v);
+  if constexpr (LPG == 16) v += xor_lane<8>(v);
+  return v;
+}
+
+template <int M, bool DALIGN, int EPL>
+__global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvArgs a) {
+  using C = Pq2Cfg<EPL>;
+  constexpr int GS = C::GS, D = C::D, RBR = C::RBR, LPG = C::LPG;
   constexpr int TILES = (M + 3) / 4;
+  constexpr int MPRE = EPL == 8 ? (M < 4 ? M : 4) : 1;  // activation rows loaded before the weights
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -209,33 +258,45 @@ __global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a)
   const int vg = min(max(g1 - gw, 0), GS);      // its real groups
   const int64_t kw0 = (int64_t)gw * 128;        // first element of its K-range
   uint8_t* areg = lds + wave * (GS * M * 512);  // its operand bytes
-  float* part = reinterpret_cast<float*>(lds + pq2_lds_part_offset(M, NW));
+  float* part = reinterpret_cast<float*>(lds + pq2_lds_part_offset(M, NW, GS));
 
-  const int rb0 = (int)((int64_t)blockIdx.x * a.total_rb / a.grid_x);
-  const int rb1 = (int)((int64_t)(blockIdx.x + 1) * a.total_rb / a.grid_x);
+  const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
+  const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
   const int nrb = rb1 - rb0;
 
-  // ---- activation row 0 first (the vector memory counter completes in
-  // order).  Lane l holds positions 16l .. 16l+15 of the wave's K-range: the
-  // codes of one packed word, in group l/8.
-  const bool live = (lane >> 3) < vg;
-  auto load_x = [&](int m, float (&v)[16]) {
+  // ---- activations first (the vector memory counter completes in order).
+  // Lane l holds positions EPL*l .. EPL*l + EPL-1 of the wave's K-range: all
+  // or half of one packed code word, in group l / LPG.
+  const bool live = lane / LPG < vg;
+  auto load_x = [&](int m, float (&v)[EPL]) {
     if (live) {
-      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + kw0) + 4 * lane;
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + kw0) + (EPL / 4) * lane;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < EPL / 4; ++i) {
         const float4 f = src[i];
         v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.f;
+      for (int i = 0; i < EPL; ++i) v[i] = 0.f;
     }
   };
-  float xv0[16];
-  load_x(0, xv0);
-  uint4 sg = make_uint4(0u, 0u, 0u, 0u);
-  if (live && a.signs) sg = *reinterpret_cast<const uint4*>(a.signs + kw0 + 16 * lane);
+  float xv[MPRE][EPL];
+#pragma unroll
+  for (int m = 0; m < MPRE; ++m) load_x(m, xv[m]);
+  const bool has_signs = a.signs != nullptr;
+  uint32_t sw[EPL / 4];
+#pragma unroll
+  for (int i = 0; i < EPL / 4; ++i) sw[i] = 0u;
+  if (live && has_signs) {
+    if constexpr (EPL == 8) {
+      const uint2 t = *reinterpret_cast<const uint2*>(a.signs + kw0 + 8 * lane);
+      sw[0] = t.x; sw[1] = t.y;
+    } else {
+      const uint4 t = *reinterpret_cast<const uint4*>(a.signs + kw0 + 16 * lane);
+      sw[0] = t.x; sw[1] = t.y; sw[2] = t.z; sw[3] = t.w;
+    }
+  }
 
   // ---- weight loads (pair q: groups 2q, 2q+1 of the wave)
   uint32_t qoff[GS / 2];
@@ -249,22 +310,28 @@ __global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a)
     uint4 q[GS / 2];
     uint32_t d[GS / 2];
   };
+  const int64_t wrow0 = (int64_t)rb0 * kRB;
+  int64_t wrows = a.N - wrow0;
+  wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
+  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)(wrows * a.row_bytes));
+  const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
   auto issue = [&](int j, WBuf& b) {
-    const int64_t row0 = (int64_t)(rb0 + j) * kRB;
-    int64_t rows = a.N - row0;
-    rows = rows < 0 ? 0 : (rows > kRB ? kRB : rows);
-    if (j >= nrb) rows = 0;
-    const BufRsrc rq = make_rsrc(a.qs + row0 * a.row_bytes, (uint32_t)rows * a.row_bytes);
-    const BufRsrc rd = make_rsrc(a.dpl + row0 * a.d_row_bytes, (uint32_t)rows * a.d_row_bytes);
+    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t rod = j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows;
 #pragma unroll
-    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q]);
-    if (DALIGN) {
-      const uint4 t = buffer_load_16B(rd, doff);
-      b.d[0] = t.x; b.d[1] = t.y; b.d[2] = t.z; b.d[3] = t.w;
+    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q] + ro);
+    if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
+      if constexpr (GS == 4) {
+        const uint2 t = buffer_load_8B(rd, doff + rod);
+        b.d[0] = t.x; b.d[1] = t.y;
+      } else {
+        const uint4 t = buffer_load_16B(rd, doff + rod);
+        b.d[0] = t.x; b.d[1] = t.y; b.d[2] = t.z; b.d[3] = t.w;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < GS / 2; ++i)
-        b.d[i] = buffer_load_2B(rd, doff + 4u * i) | (buffer_load_2B(rd, doff + 4u * i + 2u) << 16);
+        b.d[i] = buffer_load_2B(rd, doff + rod + 4u * i) | (buffer_load_2B(rd, doff + rod + 4u * i + 2u) << 16);
     }
   };
   WBuf wb[D];
@@ -279,32 +346,34 @@ __global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a)
 #pragma unroll
     for (int g = 0; g < GS; ++g) xr[t][g] = gsc[t][g] = 0.f;
   {
-    const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
-    const int pw = lane & 7;                         // packed word in the group
+    const int pw = (lane / C::LPW) & 7;              // packed word in the group
+    const int half = lane % C::LPW;                  // which half of it (EPL = 8)
     const int kb16 = (0x76325410 >> (4 * pw)) & 15;  // {0,1,4,5,2,3,6,7}[pw]
-    uint8_t* dst0 = areg + (lane >> 3) * M * 512 + (kb16 & 3) * 32 + (kb16 >> 2) * 16;
-    // even positions of the word become operand bytes 0..7, odd ones 8..15
-    constexpr int P[16] = {0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15};
+    // MFMA operand position of the word: even positions of the word become
+    // operand bytes 0..7, odd ones 8..15; a half word owns bytes 4*half + {0..3, 8..11}
+    uint8_t* dst0 = areg + (lane / LPG) * M * 512 + (kb16 & 3) * 32 + (kb16 >> 2) * 16 + 4 * half;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      float v[16];
-      if (m == 0) {
+      float v[EPL];
+      if (m < MPRE) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = xv0[i];
+        for (int i = 0; i < EPL; ++i) v[i] = xv[m < MPRE ? m : 0][i];
       } else {
         load_x(m, v);
       }
+      if (has_signs) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;  // int8 sign bit
-        v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (neg << 31));
+        for (int j = 0; j < EPL; ++j) {
+          const uint32_t neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;  // int8 sign bit
+          v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (neg << 31));
+        }
       }
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int st = 0; st < C::LOG_EPL; ++st) {
         if (st < a.log2n) {
           const int h = 1 << st;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
+          for (int i = 0; i < EPL; ++i)
             if ((i & h) == 0) {
               const float p0 = v[i], p1 = v[i + h];
               v[i] = p0 + p1;
@@ -312,56 +381,66 @@ __global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a)
             }
         }
       }
-      if (a.log2n > 4) lane_butterfly<1>(v);
-      if (a.log2n > 5) lane_butterfly<2>(v);
-      if (a.log2n > 6) lane_butterfly<4>(v);
-      if (a.log2n > 7) lane_butterfly<8>(v);
-      if (a.log2n > 8) lane_butterfly<16>(v);
-      if (a.log2n > 9) lane_butterfly<32>(v);
-      // range scale of this lane's 128-group (its 8 lanes)
+      cross_lane_stages<C::LOG_EPL>(v, a.log2n);
+      // range scale of this lane's 128-group
       float mx = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
-      mx = fmaxf(mx, xor_lane<1>(mx));
-      mx = fmaxf(mx, xor_lane<2>(mx));
-      mx = fmaxf(mx, xor_lane<4>(mx));
+      for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, fabsf(v[i]));
+      mx = group_max<LPG>(mx);
       const int e = range_exponent(mx * a.inv_sqrt_n);
       const float sc = ldexpf(a.inv_sqrt_n, e);
-      float r[16];
+      float r[EPL];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] = v[i] = v[i] * sc;
+      for (int i = 0; i < EPL; ++i) r[i] = v[i] = v[i] * sc;
+      // four e5m2 terms: t_k = e5m2(residual), residual -= t_k
+      // bytes 0, 1 (term_lo) or 2, 3 (term_hi) of w
+      auto term_lo = [&](int i0, int i1, int w) {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(r[i0], r[i1], w, false);
+        const f32x2 back = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+        r[i0] -= back.x;
+        r[i1] -= back.y;
+        return w;
+      };
+      auto term_hi = [&](int i0, int i1, int w) {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(r[i0], r[i1], w, true);
+        const f32x2 back = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+        r[i0] -= back.x;
+        r[i1] -= back.y;
+        return w;
+      };
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        uint32_t tw[4];
+        uint8_t* dst = dst0 + (m * 4 + t) * 128;
+        if constexpr (EPL == 8) {
+          const int we = term_hi(4, 6, term_lo(0, 2, 0));
+          const int wo = term_hi(5, 7, term_lo(1, 3, 0));
+          if (live) {
+            *reinterpret_cast<uint32_t*>(dst) = (uint32_t)we;
+            *reinterpret_cast<uint32_t*>(dst + 8) = (uint32_t)wo;
+          }
+        } else {
+          constexpr int P[16] = {0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15};
+          uint32_t tw[4];
 #pragma unroll
-        for (int dq = 0; dq < 4; ++dq) {
-          int w = __builtin_amdgcn_cvt_pk_bf8_f32(r[P[4 * dq]], r[P[4 * dq + 1]], 0, false);
-          w = __builtin_amdgcn_cvt_pk_bf8_f32(r[P[4 * dq + 2]], r[P[4 * dq + 3]], w, true);
-          tw[dq] = (uint32_t)w;
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
-          r[P[4 * dq]] -= lo.x;
-          r[P[4 * dq + 1]] -= lo.y;
-          r[P[4 * dq + 2]] -= hi.x;
-          r[P[4 * dq + 3]] -= hi.y;
+          for (int dq = 0; dq < 4; ++dq) {
+            tw[dq] = (uint32_t)term_hi(P[4 * dq + 2], P[4 * dq + 3], term_lo(P[4 * dq], P[4 * dq + 1], 0));
+          }
+          if (live) *reinterpret_cast<uint4*>(dst) = make_uint4(tw[0], tw[1], tw[2], tw[3]);
         }
-        if (live) *reinterpret_cast<uint4*>(dst0 + (m * 4 + t) * 128) = make_uint4(tw[0], tw[1], tw[2], tw[3]);
       }
       // X = sum of t0 + t1 + t2 + t3 over the group (exact per element)
       float tsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tsum += v[i] - r[i];
-      tsum += xor_lane<1>(tsum);
-      tsum += xor_lane<2>(tsum);
-      tsum += xor_lane<4>(tsum);
+      for (int i = 0; i < EPL; ++i) tsum += v[i] - r[i];
+      tsum = group_sum<LPG>(tsum);
       const float inv = ldexpf(1.f, -e);
       const float xs = tsum * inv;
       // the lanes whose outputs belong to activation row m take X and 2^-e of
       // every group from the group's first lane
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        const float xg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xs), 8 * g));
-        const float ig = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), 8 * g));
+        const float xg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xs), LPG * g));
+        const float ig = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), LPG * g));
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
           if (4 * t + kb == m && g < vg) {
@@ -414,12 +493,12 @@ __global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a)
       Y[t] = zero;
       cr[t] = 0.f;
     }
-    // Two halves of four groups.  The accumulators are read only after a
-    // delay that is tied to them as asm operands: the compiler's wait-state
-    // count for this mixed e5m2 x fp4 MFMA was measured to be too short on
-    // gfx950, and the B registers stay untouched until the delay has passed.
+    // Blocks of four groups.  The accumulators are read only after a delay
+    // that is tied to them as asm operands: the compiler's wait-state count
+    // for this mixed e5m2 x fp4 MFMA was measured to be too short on gfx950,
+    // and the B registers stay untouched until the delay has passed.
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < GS / 4; ++h) {
       i32x8 Bq[4];
       f32x4 acc[TILES][4];
 #pragma unroll
@@ -468,6 +547,15 @@ __global__ __launch_bounds__(Pq2Cfg::MAXW * 64) void gemv_pq2_kernel(GemvArgs a)
     }
   };
 
+  if (nrb <= D) {
+    // every row block is already in flight: no further loads
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i < nrb) compute(wb[i], i);
+    __syncthreads();
+    reduce_round(a, part, NW, RBR, M, rb0, nrb, 0, blockIdx.y);
+    return;
+  }
   for (int j0 = 0; j0 < nrb; j0 += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -559,8 +647,8 @@ __global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
   float* xs = reinterpret_cast<float*>(lds);  // [M][KRmax]
   float* part = reinterpret_cast<float*>(lds + q8_lds_part_offset(M, NW));
 
-  const int rb0 = (int)((int64_t)blockIdx.x * a.total_rb / a.grid_x);
-  const int rb1 = (int)((int64_t)(blockIdx.x + 1) * a.total_rb / a.grid_x);
+  const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
+  const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
   const int nrb = rb1 - rb0;
 
   // ---- activation loads first (rows past the first four after the weight
@@ -600,32 +688,33 @@ __global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
     uint4 q[GS / 2];
     uint32_t d[DW];
   };
+  const int64_t wrow0 = (int64_t)rb0 * kRB;
+  int64_t wrows = a.N - wrow0;
+  wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
+  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)(wrows * a.row_bytes));
+  const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
   auto issue = [&](int j, WBuf& b) {
-    const int64_t row0 = (int64_t)(rb0 + j) * kRB;
-    int64_t rows = a.N - row0;
-    rows = rows < 0 ? 0 : (rows > kRB ? kRB : rows);
-    if (j >= nrb) rows = 0;
-    const BufRsrc rq = make_rsrc(a.qs + row0 * a.row_bytes, (uint32_t)rows * a.row_bytes);
-    const BufRsrc rd = make_rsrc(a.dpl + row0 * a.d_row_bytes, (uint32_t)rows * a.d_row_bytes);
+    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t dro = (j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows) + doff;
 #pragma unroll
-    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q]);
+    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q] + ro);
     if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
 #pragma unroll
       for (int i = 0; i < DW / 4; ++i) {
-        const uint4 t = buffer_load_16B(rd, doff + 16u * i);
+        const uint4 t = buffer_load_16B(rd, dro + 16u * i);
         b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
       }
       if (DW % 4 >= 2) {
-        const uint2 t = buffer_load_8B(rd, doff + 16u * (DW / 4));
+        const uint2 t = buffer_load_8B(rd, dro + 16u * (DW / 4));
         b.d[DW / 4 * 4] = t.x; b.d[DW / 4 * 4 + 1] = t.y;
       }
       if (DW % 2)
-        b.d[DW - 1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(doff + 4u * (DW - 1)), 0, 0);
+        b.d[DW - 1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(dro + 4u * (DW - 1)), 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < DW; ++i) {
-        const uint32_t lo = buffer_load_2B(rd, doff + 4u * i);
-        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, doff + 4u * i + 2u) : 0u;
+        const uint32_t lo = buffer_load_2B(rd, dro + 4u * i);
+        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, dro + 4u * i + 2u) : 0u;
         b.d[i] = lo | (hi << 16);
       }
     }
@@ -770,10 +859,12 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   p.split = -1;
   const bool pq2 = fmt == kFmtPQ2;
   const int GROUP = pq2 ? 128 : 32;
-  const int GS = pq2 ? Pq2Cfg::GS : Q8Cfg::GS;
-  const int MAXW = pq2 ? Pq2Cfg::MAXW : Q8Cfg::MAXW;
-  const int G = (int)(K / GROUP);
   const int n = block_len > 1 ? block_len : 1;
+  // PQ2_0: half-word lanes unless a rotation block needs a whole wave
+  const int epl = pq2 ? (n <= 512 ? 8 : 16) : 0;
+  const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : Q8Cfg::GS;
+  const int MAXW = pq2 ? (epl == 8 ? Pq2Cfg<8>::MAXW : Pq2Cfg<16>::MAXW) : Q8Cfg::MAXW;
+  const int G = (int)(K / GROUP);
   const int U = n > GROUP ? n / GROUP : 1;
   const int NU = G / U;
   auto waves_for = [&](int S) {
@@ -782,7 +873,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   };
   auto lds_for = [&](int S) {
     const int nw = waves_for(S);
-    return pq2 ? pq2_lds_bytes((int)M, nw) : q8_lds_bytes((int)M, nw);
+    return pq2 ? pq2_lds_bytes((int)M, nw, GS) : q8_lds_bytes((int)M, nw);
   };
   auto fits = [&](int S) { return waves_for(S) <= MAXW && lds_for(S) <= kLdsBudget; };
   int S;
@@ -795,16 +886,24 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
     if (S > NU) return p;
   }
   p.split = S;
+  p.epl = epl;
   p.units = U;
   p.nw = waves_for(S);
   p.lds_bytes = lds_for(S);
   p.total_rb = (int)((N + kRB - 1) / kRB);
   const int target = kTargetWGs / S > 0 ? kTargetWGs / S : 1;
   p.grid_x = p.total_rb < target ? p.total_rb : target;
+  // a workgroup's rows must fit its buffer resources (see kFarRows)
+  const int64_t row_bytes = pq2 ? K / 4 : K;
+  const int64_t wg_rb = (p.total_rb + p.grid_x - 1) / p.grid_x;
+  if (wg_rb * kRB * row_bytes > kMaxWgBytes) {
+    p.split = -1;
+    return p;
+  }
   // scale runs of a wave start on a 4-byte boundary when every slice starts
   // on an even group and rows hold an even number of groups
   bool even = G % 2 == 0;
-  for (int s = 0; s < S && even; ++s) even = ((int64_t)s * NU / S * U) % 2 == 0;
+  for (int s = 0; s < S && even; ++s) even = part_start(s, NU / S, NU % S) * U % 2 == 0;
   p.dalign = even;
   return p;
 }
@@ -829,9 +928,13 @@ static int launch_kernel(Kernel k, const GemvArgs& a, const GemvPlan& p, hipStre
 
 template <int M>
 static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
-  if (fmt == kFmtPQ2)
-    return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true>, a, p, st)
-                    : launch_kernel(gemv_pq2_kernel<M, false>, a, p, st);
+  if (fmt == kFmtPQ2) {
+    if (p.epl == 8)
+      return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 8>, a, p, st)
+                      : launch_kernel(gemv_pq2_kernel<M, false, 8>, a, p, st);
+    return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 16>, a, p, st)
+                    : launch_kernel(gemv_pq2_kernel<M, false, 16>, a, p, st);
+  }
   return p.dalign ? launch_kernel(gemv_q8_kernel<M, true>, a, p, st)
                   : launch_kernel(gemv_q8_kernel<M, false>, a, p, st);
 }
@@ -856,6 +959,10 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
   a.S = p.split;
   a.total_rb = p.total_rb;
   a.grid_x = p.grid_x;
+  a.rb_base = p.total_rb / p.grid_x;
+  a.rb_rem = p.total_rb % p.grid_x;
+  a.u_base = (a.G / p.units) / p.split;
+  a.u_rem = (a.G / p.units) % p.split;
   int log2n = 0;
   while (block_len > 1 && (1 << log2n) < block_len) ++log2n;
   a.log2n = log2n;

@@ -138,10 +138,13 @@ size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N,
  * (deterministic, no atomics); 0 = chosen by the library.  Results are
  * bitwise reproducible for a given (split_k, M, N, K).
  * workspace: at least kq_workspace_bytes(0, ...) bytes of device memory
- * (x' and split partials), or NULL when that is 0.
+ * (the split partials), or NULL when that is 0.
  * Errors: KQ_EINVAL, KQ_ESHAPE (M not in 1..8, N < 1, K not a multiple of
  * the block, bad block_len, split_k < 0 or larger than K's block count),
- * KQ_EALIGN, KQ_EWORKSPACE, KQ_EDEVICE. */
+ * KQ_EALIGN, KQ_EWORKSPACE, KQ_EDEVICE; KQ_EUNSUPPORTED when no launch plan
+ * fits: more K slices than rotation blocks, a K slice too wide for one
+ * workgroup's LDS, or more than 512 MiB of packed codes per workgroup (a
+ * workgroup streams about 1/256 of the rows). */
 kq_status kq_gemv(kq_format fmt, const void *packed, int64_t N, int64_t K,
                   const float *x, int64_t M, int32_t block_len,
                   const int8_t *signs, int32_t split_k, float *y,
