@@ -91,7 +91,8 @@ __global__ __launch_bounds__(256, 2) void gemm_pq2_kernel(GemmArgs a) {
   const int64_t am = m0 + lr, bn = n0 + lr;
   const bool a_ok = am < a.M, b_ok = bn < a.N;
   const uint16_t* a_src = a.xb + am * a.K + lh * 32;
-  const uint8_t* b_src = a.qs + bn * a.row_bytes + lh * 8;
+  // codes of row bn: tile (bn / 16, k / 128), row bn % 16 at 32 bytes each
+  const uint8_t* b_src = a.qs + (bn >> 4) * (a.d_per_row * 512) + (bn & 15) * 32 + lh * 8;
   const uint16_t* d_src = a.dpl + bn * a.d_per_row;
 
   uint4 ra[4];
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void gemm_pq2_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) ra[i] = make_uint4(0u, 0u, 0u, 0u);
     }
     if (b_ok) {
-      rq = *reinterpret_cast<const uint2*>(b_src + k0 / 4);
+      rq = *reinterpret_cast<const uint2*>(b_src + (k0 >> 7) * 512 + ((k0 & 127) >> 2));
       rd = f16_bits_to_f32(d_src[k0 >> 7]);
     } else {
       rq = make_uint2(0x55555555u, 0x55555555u);

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 #pragma unroll
   for (int q = 0; q < GS / 2; ++q) {
     const int grp = 2 * q + (kb >> 1);
-    qoff[q] = grp < vg ? (uint32_t)r16 * a.row_bytes + (uint32_t)gw * 32u + 64u * q + 16u * kb : kOutOfRange;
+    qoff[q] = grp < vg ? (uint32_t)(gw + grp) * 512u + 32u * r16 + 16u * (kb & 1) : kOutOfRange;
   }
   const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)gw * 2u;
   struct WBuf {
@@ -313,7 +313,8 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   int64_t wrows = a.N - wrow0;
   wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
-  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)(wrows * a.row_bytes));
+  // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
+  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
@@ -680,8 +681,7 @@ __global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
 #pragma unroll
   for (int q = 0; q < GS / 2; ++q) {
     const int grp = 2 * q + (kb >> 1);
-    qoff[q] = grp < vg ? (uint32_t)r16 * a.row_bytes + (uint32_t)(g0 + gw) * 32u + 64u * q + 16u * kb
-                       : kOutOfRange;
+    qoff[q] = grp < vg ? (uint32_t)(g0 + gw + grp) * 512u + 32u * r16 + 16u * (kb & 1) : kOutOfRange;
   }
   const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)(g0 + gw) * 2u;
   struct WBuf {
@@ -691,7 +691,8 @@ __global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   int64_t wrows = a.N - wrow0;
   wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
-  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)(wrows * a.row_bytes));
+  // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
+  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;

@@ -75,6 +75,14 @@ __device__ __forceinline__ float group_sum_pow2(float v, int n) {
 // Raw buffer access (gfx9 buffer resource, stride 0): loads whose byte offset
 // lies outside [0, num_bytes) return zero instead of touching memory.
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
+// Code plane tiling: the 32 code bytes of block b of row n live in tile
+// (n / 16, b) -- 16 rows x 32 bytes, row n % 16 at byte 32 * (n % 16) -- and
+// tile (t, b) starts at byte 512 * (t * nb + b).  A pair of blocks of a
+// 16-row block is then 1 KiB of contiguous memory.  Word index of 32-bit word
+// wr (of K/16 or K/4 per row) of row n, for nb blocks per row:
+__host__ __device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t wr, int64_t nb) {
+  return (((n >> 4) * nb + (wr >> 3)) << 7) + ((n & 15) << 3) + (wr & 7);
+}
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;  // an offset past any range used here
 __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,

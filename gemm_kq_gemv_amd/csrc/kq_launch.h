@@ -15,8 +15,8 @@ inline int group_of(int fmt) { return fmt == kFmtPQ2 ? 128 : 32; }
 struct PlanarView {
   uint8_t* qs;
   uint8_t* d;
-  int64_t qs_bytes;    // N * K/4 (PQ2_0) or N * K (Q8_0)
-  int64_t row_bytes;   // qs bytes per row
+  int64_t qs_bytes;    // code plane: whole 16-row tiles, ceil(N/16)*16 * row_bytes
+  int64_t row_bytes;   // code bytes per row (32 per block)
   int64_t d_per_row;   // scales per row
   int64_t total_bytes;
 };
@@ -24,7 +24,7 @@ struct PlanarView {
 inline PlanarView planar_view(int fmt, int64_t N, int64_t K, void* base) {
   PlanarView v;
   v.row_bytes = fmt == kFmtPQ2 ? K / 4 : K;
-  v.qs_bytes = N * v.row_bytes;
+  v.qs_bytes = (N + 15) / 16 * 16 * v.row_bytes;
   int64_t d_off = (v.qs_bytes + 255) / 256 * 256;
   v.d_per_row = K / group_of(fmt);
   v.total_bytes = d_off + N * v.d_per_row * 2;

@@ -8,11 +8,13 @@
 // division is the IEEE one, and an all-zero group keeps d = 0 with the
 // neutral code (1 for PQ2_0, 0 for Q8_0).
 //
-// Launch shape: one thread per 32-bit word of the qs plane.  For PQ2_0 a
-// word holds 16 codes and 8 consecutive threads cover one 128-group; for
-// Q8_0 a word holds 4 int8 and 8 threads cover one 32-group.  The group max
-// is reduced across those 8 lanes with xor shuffles, so one pass reads W once
-// with coalesced 64/16-byte loads and writes the plane with coalesced dwords.
+// Launch shape: one thread per 32-bit code word, in row-major order over the
+// rows padded to whole 16-row tiles.  For PQ2_0 a word holds 16 codes and 8
+// consecutive threads cover one 128-group; for Q8_0 a word holds 4 int8 and 8
+// threads cover one 32-group.  The group max is reduced across those 8 lanes
+// with xor shuffles, so one pass reads W once with coalesced 64/16-byte loads;
+// each group's 8 words land as 32 contiguous bytes of its tile, and padding
+// rows are written as zeros.
 #include "kq_device.h"
 #include "kq_launch.h"
 
@@ -28,9 +30,10 @@ __device__ __forceinline__ float group8_max(float a) {
 
 __global__ __launch_bounds__(256) void pack_pq2_kernel(
     const float* __restrict__ W, uint32_t* __restrict__ qs, uint16_t* __restrict__ dplane,
-    int64_t n_words) {
+    int64_t n_words, int64_t live_words, int64_t words_per_row) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  bool live = g < n_words;
+  const bool in_plane = g < n_words;
+  bool live = g < live_words;
   float w[16];
   if (live) {
     const float4* src = reinterpret_cast<const float4*>(W) + g * 4;
@@ -59,17 +62,18 @@ __global__ __launch_bounds__(256) void pack_pq2_kernel(
     }
     word |= (uint32_t)q << (2 * j);
   }
-  if (live) {
-    qs[g] = word;
-    if ((g & 7) == 0) dplane[g >> 3] = d16;
+  if (in_plane) {
+    qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? word : 0u;
+    if (live && (g & 7) == 0) dplane[g >> 3] = d16;
   }
 }
 
 __global__ __launch_bounds__(256) void pack_q8_kernel(
     const float* __restrict__ W, uint32_t* __restrict__ qs, uint16_t* __restrict__ dplane,
-    int64_t n_words) {
+    int64_t n_words, int64_t live_words, int64_t words_per_row) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  bool live = g < n_words;
+  const bool in_plane = g < n_words;
+  bool live = g < live_words;
   float4 v = live ? reinterpret_cast<const float4*>(W)[g] : make_float4(0.f, 0.f, 0.f, 0.f);
   float w[4] = {v.x, v.y, v.z, v.w};
   float amax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
@@ -87,19 +91,19 @@ __global__ __launch_bounds__(256) void pack_q8_kernel(
     }
     word |= ((uint32_t)q & 0xFFu) << (8 * j);
   }
-  if (live) {
-    qs[g] = word;
-    if ((g & 7) == 0) dplane[g >> 3] = d16;
+  if (in_plane) {
+    qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? word : 0u;
+    if (live && (g & 7) == 0) dplane[g >> 3] = d16;
   }
 }
 
-// Dequantize: one thread per 32-bit qs word.
+// Dequantize: one thread per 32-bit code word of the N real rows (row-major).
 __global__ __launch_bounds__(256) void unpack_pq2_kernel(
     const uint32_t* __restrict__ qs, const uint16_t* __restrict__ dplane,
-    float* __restrict__ W, int64_t n_words) {
+    float* __restrict__ W, int64_t n_words, int64_t words_per_row) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_words) return;
-  uint32_t word = qs[g];
+  uint32_t word = qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)];
   float d = f16_bits_to_f32(dplane[g >> 3]);
   float4* dst = reinterpret_cast<float4*>(W) + g * 4;
 #pragma unroll
@@ -113,10 +117,10 @@ __global__ __launch_bounds__(256) void unpack_pq2_kernel(
 
 __global__ __launch_bounds__(256) void unpack_q8_kernel(
     const uint32_t* __restrict__ qs, const uint16_t* __restrict__ dplane,
-    float* __restrict__ W, int64_t n_words) {
+    float* __restrict__ W, int64_t n_words, int64_t words_per_row) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_words) return;
-  uint32_t word = qs[g];
+  uint32_t word = qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)];
   float d = f16_bits_to_f32(dplane[g >> 3]);
   float v[4];
 #pragma unroll
@@ -129,24 +133,24 @@ static int blocks_for(int64_t n) { return (int)((n + 255) / 256); }
 int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed,
                 hipStream_t st) {
   PlanarView pv = planar_view(fmt, N, K, packed);
-  int64_t n_words = pv.qs_bytes / 4;
+  const int64_t n_words = pv.qs_bytes / 4, wpr = pv.row_bytes / 4, live = N * wpr;
   if (n_words == 0) return 0;
   if (fmt == 1)
-    pack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words);
+    pack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr);
   else
-    pack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words);
+    pack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W,
                   hipStream_t st) {
   PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
-  int64_t n_words = pv.qs_bytes / 4;
+  const int64_t wpr = pv.row_bytes / 4, n_words = N * wpr;
   if (n_words == 0) return 0;
   if (fmt == 1)
-    unpack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words);
+    unpack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words, wpr);
   else
-    unpack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words);
+    unpack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words, wpr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -200,26 +200,30 @@ int64_t kqo_planar_bytes(int fmt, int64_t N, int64_t K)
 {
     int g = fmt_group(fmt);
     if (!g || N < 0 || K <= 0 || K % g) return -1;
-    int64_t qs_bytes = (fmt == 1) ? N * (K / 4) : N * K;
+    int64_t nb = K / g;
+    int64_t qs_bytes = (N + 15) / 16 * 16 * nb * 32;   /* whole 16-row tiles */
     int64_t d_off = (qs_bytes + 255) / 256 * 256;
-    return d_off + N * (K / g) * 2;
+    return d_off + N * nb * 2;
 }
 
+/* The 32 code bytes of block b of row n go to tile (n / 16, b): 16 rows x
+ * 32 bytes, row n % 16 at byte 32 * (n % 16), tile (t, b) at byte
+ * 512 * (t * nb + b).  Rows past N in the last tile stay zero.  The fp16
+ * scales follow at the first 256-byte boundary, [N][nb] row-major. */
 int kqo_aos_to_planar(int fmt, const uint8_t *aos, int64_t N, int64_t K,
                       uint8_t *planar)
 {
     int g = fmt_group(fmt);
     if (!g || N < 0 || K <= 0 || K % g) return -1;
     int64_t nb = K / g;
-    int64_t qs_per_block = 32;                 /* both formats: 32 qs bytes */
-    int64_t qs_bytes = N * nb * qs_per_block;
+    int64_t qs_bytes = (N + 15) / 16 * 16 * nb * 32;
     int64_t d_off = (qs_bytes + 255) / 256 * 256;
     int64_t total = kqo_planar_bytes(fmt, N, K);
     memset(planar, 0, (size_t)total);
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < nb; ++b) {
             const uint8_t *blk = aos + (n * nb + b) * 34;
-            memcpy(planar + (n * nb + b) * qs_per_block, blk + 2, 32);
+            memcpy(planar + ((n / 16) * nb + b) * 512 + (n % 16) * 32, blk + 2, 32);
             planar[d_off + (n * nb + b) * 2 + 0] = blk[0];
             planar[d_off + (n * nb + b) * 2 + 1] = blk[1];
         }

@@ -62,11 +62,13 @@ int kqo_pack_pq2_aos(const float *W, int64_t N, int64_t K, uint8_t *aos);
 int kqo_pack_q8_aos(const float *W, int64_t N, int64_t K, uint8_t *aos);
 
 /* Planar ("split") device layout of the library, restated independently:
- * the qs bytes of every block, row-major ([N][K/4] bytes for PQ2_0, [N][K]
- * for Q8_0), then, at the first 256-byte boundary after them, the fp16
- * scales row-major ([N][K/128] or [N][K/32]).  [BT 3.1 "Word view"]: the
- * codes are a reinterpretation of the qs bytes row by row and only the
- * scales move out.  fmt: 1 = PQ2_0, 2 = Q8_0. */
+ * the 32 code bytes of each block, grouped in tiles of 16 rows x one block
+ * (512 bytes; row r of the tile at byte 32*r), tiles ordered by 16-row block
+ * and then by block along K, the last tile zero-padded past row N; then, at
+ * the first 256-byte boundary after them, the fp16 scales row-major
+ * ([N][K/128] or [N][K/32]).  [BT 3.1 "Word view"]: the code bytes of a
+ * block are a reinterpretation of its qs bytes; only their place moves.
+ * fmt: 1 = PQ2_0, 2 = Q8_0. */
 int64_t kqo_planar_bytes(int fmt, int64_t N, int64_t K);
 int kqo_aos_to_planar(int fmt, const uint8_t *aos, int64_t N, int64_t K,
                       uint8_t *planar);

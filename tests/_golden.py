@@ -37,3 +37,22 @@ def sparse_block(s: str, length: int) -> np.ndarray:
         i, _, v = tok.partition("=")
         w[int(i)] = np.float32(float(v))
     return w
+
+
+def code_rows(plane, N: int, K: int, fmt: int):
+    """Row-major code bytes [N][32 * blocks] from a packed buffer: the code
+    plane holds tiles of 16 rows x 32 bytes (one block), row r of a tile at
+    byte 32 r, tiles ordered by 16-row block and then by block along K."""
+    import numpy as np
+    nb = K // (128 if fmt == 1 else 32)
+    nt = (N + 15) // 16
+    tiles = np.asarray(plane)[:nt * nb * 512].reshape(nt, nb, 16, 32)
+    return tiles.transpose(0, 2, 1, 3).reshape(nt * 16, nb * 32)[:N]
+
+
+def d_offset(N: int, K: int, fmt: int) -> int:
+    """Byte offset of the fp16 scale plane: after whole 16-row code tiles,
+    rounded up to 256."""
+    nb = K // (128 if fmt == 1 else 32)
+    qs = (N + 15) // 16 * 16 * nb * 32
+    return (qs + 255) // 256 * 256

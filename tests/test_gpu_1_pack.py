@@ -66,10 +66,10 @@ def test_pack_bit_exact(fmt, N, K):
     buf = torch.full((nbytes + 512,), 0xA5, dtype=torch.uint8, device="cuda")
     (kq.kq_pack_pq2 if fmt == 1 else kq.kq_pack_q8)(dev(W), N, K, buf)
     got = host(buf)
-    qs_bytes = N * K // 4 if fmt == 1 else N * K
-    # the bytes between the qs plane and the 256-aligned d plane are not
-    # written (the oracle zero-fills them)
-    d_off = (qs_bytes + 255) // 256 * 256
+    # whole 16-row code tiles (padding rows written as zeros); the bytes
+    # between the code plane and the 256-aligned d plane are not written
+    qs_bytes = (N + 15) // 16 * 16 * (K // 4 if fmt == 1 else K)
+    d_off = G.d_offset(N, K, fmt)
     assert np.array_equal(got[:qs_bytes], want[:qs_bytes])
     assert np.array_equal(got[d_off:nbytes], want[d_off:])
     assert np.all(got[nbytes:] == 0xA5), "write past the packed buffer"
@@ -81,17 +81,21 @@ def test_pack_golden_fixtures():
     W = np.stack([G.sparse_block(g[f"block{c}_w"], 128) for c in "ABCD"])
     packed = kq.pack(1, dev(W))
     got = host(packed)
+    rows = G.code_rows(got, 4, 128, 1)
+    d0 = G.d_offset(4, 128, 1)
     for i, c in enumerate("ABCD"):
-        assert np.array_equal(got[32 * i:32 * (i + 1)], G.hex_bytes(g[f"block{c}_qs"])), c
-        d = int(got[256 + 2 * i]) | (int(got[256 + 2 * i + 1]) << 8)
+        assert np.array_equal(rows[i], G.hex_bytes(g[f"block{c}_qs"])), c
+        d = int(got[d0 + 2 * i]) | (int(got[d0 + 2 * i + 1]) << 8)
         assert d == int(g[f"block{c}_d16"], 16), c
     g8 = G.load("q8_quantize_block.txt")
     W8 = np.stack([G.sparse_block(g8["w"], 32), G.sparse_block(g8["b2_w"], 32)])
     got8 = host(kq.pack(2, dev(W8)))
-    assert np.array_equal(got8[:32].view(np.int8).astype(np.int64), G.ints(g8["q"]))
-    assert np.array_equal(got8[32:64].view(np.int8).astype(np.int64), G.ints(g8["b2_q"]))
-    assert int(got8[256]) | (int(got8[257]) << 8) == int(g8["d16"], 16)
-    assert int(got8[258]) | (int(got8[259]) << 8) == int(g8["b2_d16"], 16)
+    rows8 = G.code_rows(got8, 2, 32, 2)
+    d8 = G.d_offset(2, 32, 2)
+    assert np.array_equal(rows8[0].view(np.int8).astype(np.int64), G.ints(g8["q"]))
+    assert np.array_equal(rows8[1].view(np.int8).astype(np.int64), G.ints(g8["b2_q"]))
+    assert int(got8[d8]) | (int(got8[d8 + 1]) << 8) == int(g8["d16"], 16)
+    assert int(got8[d8 + 2]) | (int(got8[d8 + 3]) << 8) == int(g8["b2_d16"], 16)
 
 
 @pytest.mark.parametrize("fmt", [1, 2])

@@ -158,13 +158,20 @@ def test_pq2_aos_to_planar_layout():
     W = inputs.weights(4, N, K)
     aos = oracle.pack_pq2_aos(W).reshape(N, K // 128, 34)
     pl = oracle.aos_to_planar(oracle.FMT_PQ2_0, aos, N, K)
-    qs_bytes = N * K // 4
+    # one 16-row block, 2 blocks along K: tiles of 16 rows x 32 bytes, rows
+    # past N zero
+    qs_bytes = 16 * 2 * 32
     d_off = (qs_bytes + 255) // 256 * 256
     assert pl.size == d_off + N * (K // 128) * 2
-    assert np.array_equal(pl[:qs_bytes].reshape(N, K // 128, 32), aos[:, :, 2:])
+    tiles = pl[:qs_bytes].reshape(2, 16, 32)
+    for n in range(N):
+        for b in range(2):
+            assert np.array_equal(tiles[b, n], aos[n, b, 2:])
+    assert not tiles[:, N:].any()
     assert np.array_equal(pl[d_off:].reshape(N, K // 128, 2), aos[:, :, :2])
-    # word view of the plane: element 16i + j of a row at bits 2j of LE word i
-    words = pl[:qs_bytes].view("<u4").reshape(N, K // 16)
+    # word view of a row's code bytes: element 16i + j at bits 2j of LE word i
+    row_codes = np.ascontiguousarray(tiles[:, :N].transpose(1, 0, 2)).reshape(N, K // 4)
+    words = row_codes.view("<u4").reshape(N, K // 16)
     codes = np.stack([(words >> (2 * j)) & 3 for j in range(16)], axis=-1).reshape(N, K)
     dF = pl[d_off:].view("<f2").astype(np.float64).reshape(N, K // 128)
     deq = (codes.astype(np.float64) - 1) * np.repeat(dF, 128, axis=1)
@@ -216,10 +223,12 @@ def test_q8_zero_block_and_planar():
     assert np.all(aos[0] == 0)                 # d = 0, q = 0
     assert np.all(aos[1, 0] == 0)
     pl = oracle.aos_to_planar(oracle.FMT_Q8_0, aos, N, K)
-    d_off = 256
-    assert np.array_equal(pl[:N * K].reshape(N, 2, 32), aos[:, :, 2:])
+    # one 16-row tile per block: 2 x 16 rows x 32 bytes, then the scales
+    d_off = 1024
+    tiles = pl[:d_off].reshape(2, 16, 32)
+    assert np.array_equal(tiles[:, :N].transpose(1, 0, 2), aos[:, :, 2:])
+    assert not tiles[:, N:].any()
     assert np.array_equal(pl[d_off:].reshape(N, 2, 2), aos[:, :, :2])
-    assert pl[N * K:d_off].sum() == 0
 
 
 # --------------------------------------------------------------------------
