@@ -320,7 +320,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t rod = j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows;
 #pragma unroll
-    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q] + ro);
+    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
     if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
       if constexpr (GS == 4) {
         const uint2 t = buffer_load_8B(rd, doff + rod);
@@ -698,7 +698,7 @@ __global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t dro = (j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows) + doff;
 #pragma unroll
-    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B(rq, qoff[q] + ro);
+    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
     if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
 #pragma unroll
       for (int i = 0; i < DW / 4; ++i) {

@@ -93,6 +93,13 @@ __device__ __forceinline__ uint4 buffer_load_16B(BufRsrc r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Streamed weights: the non-temporal hint (cache-policy bit 1 on gfx950)
+// keeps data that is read once from displacing reused lines in the caches.
+__device__ __forceinline__ uint4 buffer_load_16B_stream(BufRsrc r, uint32_t off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint32_t buffer_load_2B(BufRsrc r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
