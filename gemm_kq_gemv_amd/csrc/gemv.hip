@@ -574,17 +574,21 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 // ---------------------------------------------------------------------------
 // Q8_0
 
+// GS groups of 32 per wave: 10 (16 waves at K=5120, at most 128 VGPRs) for
+// one activation row; 20 (8 waves, up to 256 VGPRs) for more, where the
+// staged rows and operands no longer fit the smaller register budget.
+template <int GS_>
 struct Q8Cfg {
-  static constexpr int GS = 10;  // groups of 32 per wave
+  static constexpr int GS = GS_;
   static constexpr int D = 2;
   static constexpr int RBR = 4;
-  static constexpr int MAXW = 16;
+  static constexpr int MAXW = GS_ == 10 ? 16 : 8;
 };
 
 // LDS bytes: staged activations f32 [M][NW*GS*32], then the partials
-__host__ __device__ inline int q8_lds_part_offset(int M, int NW) { return M * NW * Q8Cfg::GS * 32 * 4; }
-__host__ __device__ inline int q8_lds_bytes(int M, int NW) {
-  return q8_lds_part_offset(M, NW) + 2 * NW * Q8Cfg::RBR * M * kRB * 4;
+__host__ __device__ inline int q8_lds_part_offset(int M, int NW, int GS) { return M * NW * GS * 32 * 4; }
+__host__ __device__ inline int q8_lds_bytes(int M, int NW, int GS) {
+  return q8_lds_part_offset(M, NW, GS) + 2 * NW * 4 * M * kRB * 4;
 }
 
 // rotation stages with h >= 16 in LDS: butterflies on E = 2^L values at stride 16
@@ -626,9 +630,9 @@ __device__ void lds_stages(float* xs, int KRmax, int KR, int log2n, int M_) {
   }
 }
 
-template <int M, bool DALIGN>
-__global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
-  constexpr int GS = Q8Cfg::GS, D = Q8Cfg::D, RBR = Q8Cfg::RBR;
+template <int M, bool DALIGN, int QGS>
+__global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
+  constexpr int GS = Q8Cfg<QGS>::GS, D = Q8Cfg<QGS>::D, RBR = Q8Cfg<QGS>::RBR;
   constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
   extern __shared__ __align__(16) uint8_t lds[];
 
@@ -646,7 +650,7 @@ __global__ __launch_bounds__(Q8Cfg::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
   const int vg = min(max(g1 - g0 - gw, 0), GS);
   const int KRmax = NW * GS * 32;
   float* xs = reinterpret_cast<float*>(lds);  // [M][KRmax]
-  float* part = reinterpret_cast<float*>(lds + q8_lds_part_offset(M, NW));
+  float* part = reinterpret_cast<float*>(lds + q8_lds_part_offset(M, NW, GS));
 
   const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
   const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
@@ -863,8 +867,10 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   const int n = block_len > 1 ? block_len : 1;
   // PQ2_0: half-word lanes unless a rotation block needs a whole wave
   const int epl = pq2 ? (n <= 512 ? 8 : 16) : 0;
-  const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : Q8Cfg::GS;
-  const int MAXW = pq2 ? (epl == 8 ? Pq2Cfg<8>::MAXW : Pq2Cfg<16>::MAXW) : Q8Cfg::MAXW;
+  const int q8gs = M == 1 ? 10 : 20;
+  const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : q8gs;
+  const int MAXW = pq2 ? (epl == 8 ? Pq2Cfg<8>::MAXW : Pq2Cfg<16>::MAXW)
+                       : (q8gs == 10 ? Q8Cfg<10>::MAXW : Q8Cfg<20>::MAXW);
   const int G = (int)(K / GROUP);
   const int U = n > GROUP ? n / GROUP : 1;
   const int NU = G / U;
@@ -874,7 +880,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   };
   auto lds_for = [&](int S) {
     const int nw = waves_for(S);
-    return pq2 ? pq2_lds_bytes((int)M, nw, GS) : q8_lds_bytes((int)M, nw);
+    return pq2 ? pq2_lds_bytes((int)M, nw, GS) : q8_lds_bytes((int)M, nw, GS);
   };
   auto fits = [&](int S) { return waves_for(S) <= MAXW && lds_for(S) <= kLdsBudget; };
   int S;
@@ -888,6 +894,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   }
   p.split = S;
   p.epl = epl;
+  p.gs = GS;
   p.units = U;
   p.nw = waves_for(S);
   p.lds_bytes = lds_for(S);
@@ -936,8 +943,10 @@ static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t s
     return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 16>, a, p, st)
                     : launch_kernel(gemv_pq2_kernel<M, false, 16>, a, p, st);
   }
-  return p.dalign ? launch_kernel(gemv_q8_kernel<M, true>, a, p, st)
-                  : launch_kernel(gemv_q8_kernel<M, false>, a, p, st);
+  constexpr int QGS = M == 1 ? 10 : 20;  // as plan_gemv chooses
+  if (p.gs != QGS) return -1;
+  return p.dalign ? launch_kernel(gemv_q8_kernel<M, true, QGS>, a, p, st)
+                  : launch_kernel(gemv_q8_kernel<M, false, QGS>, a, p, st);
 }
 
 int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,

@@ -43,6 +43,7 @@ int launch_hadamard(const void* x, int x_bf16, void* xr, int xr_bf16, int64_t M,
 struct GemvPlan {
   int split;      // S >= 1 K-slices (grid.y); < 1 if no plan fits
   int epl;        // PQ2_0 prologue: activation elements per lane (8 or 16)
+  int gs;         // groups per wave
   int units;      // groups per rotation block (slices hold whole blocks)
   int nw;         // waves per workgroup
   int grid_x;     // workgroups along the rows
