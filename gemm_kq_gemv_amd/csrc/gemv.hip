@@ -130,10 +130,13 @@ __device__ __forceinline__ void lane_butterfly(float (&v)[NV]) {
   for (int i = 0; i < NV; ++i) v[i] = fmaf(sgn, v[i], xor_lane<DIST>(v[i]));
 }
 
-// power-of-two exponent e that puts bound * 2^e in [2^14, 2^15)
+// power-of-two exponent e that puts bound * 2^e in [2^14, 2^15), read from
+// the binary32 exponent field (a subnormal bound takes the maximum e; zero,
+// infinity and NaN give 0)
 __device__ __forceinline__ int range_exponent(float bound) {
-  if (!(bound > 0.f) || !(bound < INFINITY)) return 0;
-  const int e = 14 - ilogbf(bound);
+  const uint32_t ef = (__float_as_uint(bound) >> 23) & 0xFFu;
+  if (!(bound > 0.f) || ef == 0xFFu) return 0;
+  const int e = 14 - ((int)ef - 127);
   return e < -100 ? -100 : (e > 100 ? 100 : e);
 }
 
