@@ -29,16 +29,24 @@
  *   y [M][N].  N counts output rows, K is the reduction (the page's "ne
  *   order, K first").
  * Packed weights (planar device layout).  kq_packed_bytes(fmt, N, K) bytes:
- *     qs plane : the 32 code bytes of every block, row-major, blocks in K
- *                order -- [N][K/4] bytes for PQ2_0, [N][K] int8 for Q8_0.
- *                For PQ2_0, reading 4 bytes as a little-endian u32 gives
- *                word i of a row holding element 16*i + j at bits 2*j
- *                ([BT] 3.1 "Word view").
+ *     qs plane : the 32 code bytes of every block (nb blocks per row:
+ *                K/128 for PQ2_0, K/32 for Q8_0), in tiles of 16 rows x
+ *                one block: tile (t, b) holds block b of rows 16t..16t+15
+ *                and starts at byte 512 * (t * nb + b); inside it, row
+ *                n % 16 occupies bytes 32 * (n % 16) .. +31.  Rows past N
+ *                in the last tile are zero.  Plane size:
+ *                ceil(N/16) * 16 * nb * 32 bytes.  Inside a block the 32
+ *                bytes are those of the GGUF-style block: for PQ2_0,
+ *                reading 4 bytes as a little-endian u32 gives word i of the
+ *                block holding element 16*i + j at bits 2*j ([BT] 3.1
+ *                "Word view"); for Q8_0 they are the 32 int8 codes.
  *     d plane  : at byte offset round_up(qs plane size, 256): one IEEE
- *                binary16 scale per block, [N][K/128] (PQ2_0) or [N][K/32]
- *                (Q8_0), little endian.
+ *                binary16 scale per block, [N][nb], row-major, little
+ *                endian.
  *   This is a lossless re-arrangement of the GGUF-style array of 34-byte
- *   blocks { fp16 d; uint8 qs[32] }: only the scales move out.
+ *   blocks { fp16 d; uint8 qs[32] }: the scales move out and the code
+ *   blocks of 16 rows are interleaved, so that a wave's 16 rows x 2 blocks
+ *   are one contiguous KiB.
  * Alignment.  All pointers must be 16-byte aligned, else KQ_EALIGN.
  * Errors.  Arguments are validated before anything is enqueued; on any
  *   error nothing is launched and no output byte is written.  A failed

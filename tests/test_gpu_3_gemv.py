@@ -126,7 +126,7 @@ def test_ragged_shapes(fmt, N, K):
     assert_within_bound(_run(fmt, W, x, bl, s), y_ref, b, TOL, f"{fmt} {N}x{K}")
 
 
-@pytest.mark.parametrize("block_len", [0, 2, 64, 256, 1024])
+@pytest.mark.parametrize("block_len", [0, 2, 8, 64, 128, 256, 512, 1024])
 def test_block_lengths(block_len):
     N, K = 256, 5120
     W = inputs.weights(700, N, K)
@@ -134,6 +134,20 @@ def test_block_lengths(block_len):
     s = inputs.signs(702, K) if block_len in (0, 1024) else None
     y_ref, b = _oracle_ref(1, W, x, block_len, s)
     assert_within_bound(_run(1, W, x, block_len, s), y_ref, b, TOL, f"n={block_len}")
+
+
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("block_len", [128, 1024])
+def test_q8_rotation_blocks(M, block_len):
+    """Q8_0 with a rotation: one activation row (16-wave shape) and several
+    (8-wave shape), blocks that stay inside a wave and blocks that span
+    waves."""
+    N, K = 200, 5120
+    W = inputs.weights(710 + M, N, K)
+    x = inputs.activations(711 + M, M, K)
+    s = inputs.signs(712, K)
+    y_ref, b = _oracle_ref(2, W, x, block_len, s)
+    assert_within_bound(_run(2, W, x, block_len, s), y_ref, b, TOL, f"q8 n={block_len} M={M}")
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
