@@ -130,6 +130,52 @@ __device__ __forceinline__ void lane_butterfly(float (&v)[NV]) {
   for (int i = 0; i < NV; ++i) v[i] = fmaf(sgn, v[i], xor_lane<DIST>(v[i]));
 }
 
+// The same butterfly at distance 4 or 8, where the lower and the upper lanes
+// of each pair fall in different DPP banks (groups of 4 lanes of a row): a
+// bank-masked add writes the lower lanes (partner + own) and a bank-masked
+// subtract the upper ones (partner - own), two instructions per value.  The
+// compiler inserts no hazard wait states around inline assembly, so each block
+// brings its own: a DPP read of a register written by the vector ALU needs two.
+template <int DIST, int NV>
+__device__ __forceinline__ void bank_butterfly(float (&v)[NV]) {
+  static_assert(DIST == 4 || DIST == 8, "bank-masked butterflies pair lanes 4 or 8 apart");
+  static_assert(NV % 4 == 0, "blocks of four values");
+#pragma unroll
+  for (int i = 0; i < NV; i += 4) {
+    float r0, r1, r2, r3;
+    if constexpr (DIST == 4) {
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_add_f32_dpp %0, %4, %4 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+          "v_add_f32_dpp %1, %5, %5 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+          "v_add_f32_dpp %2, %6, %6 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+          "v_add_f32_dpp %3, %7, %7 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+          "v_sub_f32_dpp %0, %4, %4 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+          "v_sub_f32_dpp %1, %5, %5 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+          "v_sub_f32_dpp %2, %6, %6 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+          "v_sub_f32_dpp %3, %7, %7 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+          "s_nop 1"
+          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+          : "v"(v[i]), "v"(v[i + 1]), "v"(v[i + 2]), "v"(v[i + 3]));
+    } else {
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_add_f32_dpp %0, %4, %4 row_shl:8 row_mask:0xf bank_mask:0x3\n\t"
+          "v_add_f32_dpp %1, %5, %5 row_shl:8 row_mask:0xf bank_mask:0x3\n\t"
+          "v_add_f32_dpp %2, %6, %6 row_shl:8 row_mask:0xf bank_mask:0x3\n\t"
+          "v_add_f32_dpp %3, %7, %7 row_shl:8 row_mask:0xf bank_mask:0x3\n\t"
+          "v_sub_f32_dpp %0, %4, %4 row_shr:8 row_mask:0xf bank_mask:0xc\n\t"
+          "v_sub_f32_dpp %1, %5, %5 row_shr:8 row_mask:0xf bank_mask:0xc\n\t"
+          "v_sub_f32_dpp %2, %6, %6 row_shr:8 row_mask:0xf bank_mask:0xc\n\t"
+          "v_sub_f32_dpp %3, %7, %7 row_shr:8 row_mask:0xf bank_mask:0xc\n\t"
+          "s_nop 1"
+          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+          : "v"(v[i]), "v"(v[i + 1]), "v"(v[i + 2]), "v"(v[i + 3]));
+    }
+    v[i] = r0; v[i + 1] = r1; v[i + 2] = r2; v[i + 3] = r3;
+  }
+}
+
 // power-of-two exponent e that puts bound * 2^e in [2^14, 2^15), read from
 // the binary32 exponent field (a subnormal bound takes the maximum e; zero,
 // infinity and NaN give 0)
@@ -208,37 +254,77 @@ struct Pq2Cfg {
 };
 
 // LDS bytes: per wave [GS][M][4 terms][4 kb][32 B] operand bytes, then the
-// partials [2][NW][RBR][M][16] floats
+// partials [2][NW][RBR][M][16] floats, then 32 zero bytes (the operand of
+// unused rows and groups)
 __host__ __device__ inline int pq2_lds_part_offset(int M, int NW, int GS) { return NW * GS * M * 512; }
-__host__ __device__ inline int pq2_lds_bytes(int M, int NW, int GS) {
+__host__ __device__ inline int pq2_lds_zero_offset(int M, int NW, int GS) {
   return pq2_lds_part_offset(M, NW, GS) + 2 * NW * 8 * M * kRB * 4;
 }
+__host__ __device__ inline int pq2_lds_bytes(int M, int NW, int GS) { return pq2_lds_zero_offset(M, NW, GS) + 32; }
 
-// butterflies of the element bits above the in-lane ones (lane distance 1..32)
-template <int LOG_EPL, int NV>
-__device__ __forceinline__ void cross_lane_stages(float (&v)[NV], int log2n) {
-  if (log2n > LOG_EPL) lane_butterfly<1>(v);
-  if (log2n > LOG_EPL + 1) lane_butterfly<2>(v);
-  if (log2n > LOG_EPL + 2) lane_butterfly<4>(v);
-  if (log2n > LOG_EPL + 3) lane_butterfly<8>(v);
-  if (log2n > LOG_EPL + 4) lane_butterfly<16>(v);
-  if (log2n > LOG_EPL + 5) lane_butterfly<32>(v);
+// Unnormalised Sylvester transform of 2^L consecutive elements held by
+// 2^(L - LOG_EPL) lanes, 2^LOG_EPL per lane: the element bits inside a lane
+// first, then those across lanes (distance 1..32).  Stages of a transform
+// commute, so any order gives H_n.
+template <int LOG_EPL, int L, int NV>
+__device__ __forceinline__ void rotate_fixed(float (&v)[NV]) {
+  constexpr int IN = L < LOG_EPL ? L : LOG_EPL;
+#pragma unroll
+  for (int st = 0; st < IN; ++st) {
+    const int h = 1 << st;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if ((i & h) == 0) {
+        const float p0 = v[i], p1 = v[i + h];
+        v[i] = p0 + p1;
+        v[i + h] = p0 - p1;
+      }
+  }
+  if constexpr (L > LOG_EPL) lane_butterfly<1>(v);
+  if constexpr (L > LOG_EPL + 1) lane_butterfly<2>(v);
+  if constexpr (L > LOG_EPL + 2) bank_butterfly<4>(v);
+  if constexpr (L > LOG_EPL + 3) bank_butterfly<8>(v);
+  if constexpr (L > LOG_EPL + 4) lane_butterfly<16>(v);
+  if constexpr (L > LOG_EPL + 5) lane_butterfly<32>(v);
 }
-// max / sum over the LPG lanes of one 128-group
+// run-time block length: one branch, then a straight-line transform
+template <int LOG_EPL, int NV>
+__device__ __forceinline__ void rotate(float (&v)[NV], int log2n) {
+  switch (log2n) {
+    case 1: rotate_fixed<LOG_EPL, 1>(v); break;
+    case 2: rotate_fixed<LOG_EPL, 2>(v); break;
+    case 3: rotate_fixed<LOG_EPL, 3>(v); break;
+    case 4: rotate_fixed<LOG_EPL, 4>(v); break;
+    case 5: rotate_fixed<LOG_EPL, 5>(v); break;
+    case 6: rotate_fixed<LOG_EPL, 6>(v); break;
+    case 7: rotate_fixed<LOG_EPL, 7>(v); break;
+    case 8: rotate_fixed<LOG_EPL, 8>(v); break;
+    case 9: rotate_fixed<LOG_EPL, 9>(v); break;
+    case 10: if constexpr (LOG_EPL + 6 >= 10) rotate_fixed<LOG_EPL, 10>(v); break;
+    default: break;  // 0: no transform
+  }
+}
+// max (of values >= 0) / sum over the LPG lanes of one 128-group (8 lanes:
+// a half row, 16: a row).  Pairs: xor 1, xor 2 within quads, then the half-row
+// and row mirrors (lane i with 7 - i, 15 - i), which pair each quad with the
+// other quad and each half with the other half; both lanes of a pair add the
+// same two values, so every lane ends with the same bits.  Non-negative
+// binary32 values order like their bit patterns, so the max is an integer one.
 template <int LPG>
 __device__ __forceinline__ float group_max(float v) {
-  v = fmaxf(v, xor_lane<1>(v));
-  v = fmaxf(v, xor_lane<2>(v));
-  v = fmaxf(v, xor_lane<4>(v));
-  if constexpr (LPG == 16) v = fmaxf(v, xor_lane<8>(v));
-  return v;
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));
+  if constexpr (LPG == 16) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));
+  return __uint_as_float(u);
 }
 template <int LPG>
 __device__ __forceinline__ float group_sum(float v) {
-  v += xor_lane<1>(v);
-  v += xor_lane<2>(v);
-  v += xor_lane<4>(v);
-  if constexpr (LPG == 16) v += xor_lane<8>(v);
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  if constexpr (LPG == 16) v += dpp<0x140>(v);
   return v;
 }
 
@@ -338,9 +424,12 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
         b.d[i] = buffer_load_2B(rd, doff + rod + 4u * i) | (buffer_load_2B(rd, doff + rod + 4u * i + 2u) << 16);
     }
   };
+  // Only the first row block is loaded before the prologue.  A wave stalls at a
+  // load it cannot issue while the compute unit's memory pipeline is full, and
+  // a stalled wave does no arithmetic; with all D blocks issued here the waves
+  // sat through the fetch and rotated x only afterwards.
   WBuf wb[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) issue(i, wb[i]);
+  issue(0, wb[0]);
 
   // ---- per-wave prologue: rotation, per-group range scale, e5m2 terms
   float xr[TILES][GS];   // X * 2^-e of (activation row 4*tile + kb, group)
@@ -372,20 +461,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
           v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (neg << 31));
         }
       }
-#pragma unroll
-      for (int st = 0; st < C::LOG_EPL; ++st) {
-        if (st < a.log2n) {
-          const int h = 1 << st;
-#pragma unroll
-          for (int i = 0; i < EPL; ++i)
-            if ((i & h) == 0) {
-              const float p0 = v[i], p1 = v[i + h];
-              v[i] = p0 + p1;
-              v[i + h] = p0 - p1;
-            }
-        }
-      }
-      cross_lane_stages<C::LOG_EPL>(v, a.log2n);
+      rotate<C::LOG_EPL>(v, a.log2n);
       // range scale of this lane's 128-group
       float mx = 0.f;
 #pragma unroll
@@ -454,9 +530,17 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
       }
     }
   }
-  // The operand bytes were written by other lanes of this wave; LDS
-  // instructions of a wave complete in order, so only the compiler must not
-  // move the reads above the writes.
+  // the other row blocks in flight (kept here by the scheduling barriers)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 1; i < D; ++i) issue(i, wb[i]);
+  __builtin_amdgcn_sched_barrier(0);
+  // Lanes of rows past M and of groups past the slice read 32 zero bytes
+  // (every wave stores the same zeros).  The operand bytes were written by
+  // other lanes of this wave; LDS instructions of a wave complete in order, so
+  // only the compiler must not move the reads above the writes.
+  uint8_t* zeros = lds + pq2_lds_zero_offset(M, NW, GS);
+  if (lane < 2) *reinterpret_cast<uint4*>(zeros + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -466,15 +550,11 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     const int ma = 4 * t + (r16 >> 2);  // activation row of this lane's operand row
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
-      if (ma < M && g < vg) {
-        const uint4* p = reinterpret_cast<const uint4*>(areg + ((g * M + ma) * 4 + (r16 & 3)) * 128 + kb * 32);
-        const uint4 p0 = p[0], p1 = p[1];
-        aop[t][g][0] = p0.x; aop[t][g][1] = p0.y; aop[t][g][2] = p0.z; aop[t][g][3] = p0.w;
-        aop[t][g][4] = p1.x; aop[t][g][5] = p1.y; aop[t][g][6] = p1.z; aop[t][g][7] = p1.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) aop[t][g][i] = 0;
-      }
+      const uint8_t* src = ma < M && g < vg ? areg + ((g * M + ma) * 4 + (r16 & 3)) * 128 + kb * 32 : zeros;
+      const uint4* p = reinterpret_cast<const uint4*>(src);
+      const uint4 p0 = p[0], p1 = p[1];
+      aop[t][g][0] = p0.x; aop[t][g][1] = p0.y; aop[t][g][2] = p0.z; aop[t][g][3] = p0.w;
+      aop[t][g][4] = p1.x; aop[t][g][5] = p1.y; aop[t][g][6] = p1.z; aop[t][g][7] = p1.w;
     }
   }
 
@@ -484,12 +564,11 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     uint2 wq[GS];
 #pragma unroll
     for (int q = 0; q < GS / 2; ++q) pair_to_operands(b.q[q], wq[2 * q], wq[2 * q + 1]);
+    // groups past the slice (g >= vg) read some other finite scale, or zero
+    // past the plane; their 2^-e and X are zero, so they add nothing
     float dg[GS];
 #pragma unroll
-    for (int g = 0; g < GS; ++g) {
-      const float dd = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
-      dg[g] = g < vg ? dd : 0.f;
-    }
+    for (int g = 0; g < GS; ++g) dg[g] = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
     f32x4 Y[TILES];
     float cr[TILES];
 #pragma unroll
