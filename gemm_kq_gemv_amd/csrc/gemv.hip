@@ -220,17 +220,19 @@ __device__ __forceinline__ void slice_groups(const GemvArgs& a, int s, int& g0, 
   g1 = part_start(s + 1, a.u_base, a.u_rem) * a.U;
 }
 
-// fixed-order sum of the wave partials of one round into y (or split partials)
+// fixed-order sum of the wave partials of one round into y (or split partials);
+// each wave leaves KS partials per output, [NW][RBR][M][KS][16]
 __device__ __forceinline__ void reduce_round(const GemvArgs& a, const float* part, int NW, int RBR,
-                                             int M, int rb0, int nrb, int round, int s) {
-  const float* pr = part + (round & 1) * NW * RBR * M * kRB;
+                                             int M, int KS, int rb0, int nrb, int round, int s) {
+  const float* pr = part + (round & 1) * NW * RBR * M * KS * kRB;
   for (int it = threadIdx.x; it < RBR * M * kRB; it += blockDim.x) {
     const int jr = it / (M * kRB), m = (it / kRB) % M, r = it % kRB;
     const int j = round * RBR + jr;
     const int64_t row = (int64_t)(rb0 + j) * kRB + r;
     if (j < nrb && row < a.N) {
       float t = 0.f;
-      for (int w = 0; w < NW; ++w) t += pr[((w * RBR + jr) * M + m) * kRB + r];
+      for (int w = 0; w < NW; ++w)
+        for (int k = 0; k < KS; ++k) t += pr[(((w * RBR + jr) * M + m) * KS + k) * kRB + r];
       a.out[((int64_t)s * M + m) * a.N + row] = t;
     }
   }
@@ -254,11 +256,13 @@ struct Pq2Cfg {
 };
 
 // LDS bytes: per wave [GS][M][4 terms][4 kb][32 B] operand bytes, then the
-// partials [2][NW][RBR][M][16] floats, then 32 zero bytes (the operand of
-// unused rows and groups)
+// partials [2][NW][RBR][M][KS][16] floats, then 32 zero bytes (the operand of
+// unused rows and groups).  KS = 4 for one activation row (the four lane
+// blocks hold one term each), else 1.
+__host__ __device__ inline int pq2_ks(int M) { return M == 1 ? 4 : 1; }
 __host__ __device__ inline int pq2_lds_part_offset(int M, int NW, int GS) { return NW * GS * M * 512; }
 __host__ __device__ inline int pq2_lds_zero_offset(int M, int NW, int GS) {
-  return pq2_lds_part_offset(M, NW, GS) + 2 * NW * 8 * M * kRB * 4;
+  return pq2_lds_part_offset(M, NW, GS) + 2 * NW * 8 * M * pq2_ks(M) * kRB * 4;
 }
 __host__ __device__ inline int pq2_lds_bytes(int M, int NW, int GS) { return pq2_lds_zero_offset(M, NW, GS) + 32; }
 
@@ -334,6 +338,12 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   constexpr int GS = C::GS, D = C::D, RBR = C::RBR, LPG = C::LPG;
   constexpr int TILES = (M + 3) / 4;
   constexpr int MPRE = EPL == 8 ? (M < 4 ? M : 4) : 1;  // activation rows loaded before the weights
+  // One activation row: operand row 4*t holds term t, so lane block kb ends
+  // with term kb of its weight row in the first accumulator, and the group's
+  // power-of-two range scale rides on the MFMA's own A scale (E8M0).  More
+  // rows: operand row 4*m + t, every accumulator used, scales applied after.
+  constexpr bool ONE = M == 1;
+  constexpr int KS = ONE ? 4 : 1;
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -432,8 +442,11 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   issue(0, wb[0]);
 
   // ---- per-wave prologue: rotation, per-group range scale, e5m2 terms
-  float xr[TILES][GS];   // X * 2^-e of (activation row 4*tile + kb, group)
+  float xr[TILES][GS];   // X * 2^-e of (activation row 4*tile + kb, group); every lane if ONE
   float gsc[TILES][GS];  // 2^-e of that (row, group)
+  int sa[GS];            // ONE: E8M0 byte of 2^-e per group
+#pragma unroll
+  for (int g = 0; g < GS; ++g) sa[g] = 127;
 #pragma unroll
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
@@ -520,13 +533,20 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
         const float xg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xs), LPG * g));
-        const float ig = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), LPG * g));
-#pragma unroll
-        for (int t = 0; t < TILES; ++t)
-          if (4 * t + kb == m && g < vg) {
-            xr[t][g] = xg;
-            gsc[t][g] = ig;
+        if constexpr (ONE) {
+          if (g < vg) {
+            xr[0][g] = xg;
+            sa[g] = 127 - __builtin_amdgcn_readlane(e, LPG * g);
           }
+        } else {
+          const float ig = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), LPG * g));
+#pragma unroll
+          for (int t = 0; t < TILES; ++t)
+            if (4 * t + kb == m && g < vg) {
+              xr[t][g] = xg;
+              gsc[t][g] = ig;
+            }
+        }
       }
     }
   }
@@ -547,10 +567,12 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   int aop[TILES][GS][8];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
-    const int ma = 4 * t + (r16 >> 2);  // activation row of this lane's operand row
+    // activation row and term of this lane's operand row
+    const int ma = ONE ? ((r16 & 3) == 0 ? 0 : M) : 4 * t + (r16 >> 2);
+    const int tm = ONE ? r16 >> 2 : r16 & 3;
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
-      const uint8_t* src = ma < M && g < vg ? areg + ((g * M + ma) * 4 + (r16 & 3)) * 128 + kb * 32 : zeros;
+      const uint8_t* src = ma < M && g < vg ? areg + ((g * M + ma) * 4 + tm) * 128 + kb * 32 : zeros;
       const uint4* p = reinterpret_cast<const uint4*>(src);
       const uint4 p0 = p[0], p1 = p[1];
       aop[t][g][0] = p0.x; aop[t][g][1] = p0.y; aop[t][g][2] = p0.z; aop[t][g][3] = p0.w;
@@ -597,7 +619,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
           const int g = 4 * h + u;
           const i32x8 A = {aop[t][g][0], aop[t][g][1], aop[t][g][2], aop[t][g][3],
                            aop[t][g][4], aop[t][g][5], aop[t][g][6], aop[t][g][7]};
-          acc[t][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq[u], zero, 1, 4, 0, 127, 0, 127);
+          acc[t][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq[u], zero, 1, 4, 0, sa[g], 0, 127);
         }
       static_assert(TILES <= 2, "the delay below lists the accumulators");
       if constexpr (TILES == 1) {
@@ -616,17 +638,26 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
           const int g = 4 * h + u;
-          const float ds = dg[g] * gsc[t][g];
+          if constexpr (ONE) {
+            Y[0][0] = fmaf(dg[g], acc[0][u][0], Y[0][0]);
+          } else {
+            const float ds = dg[g] * gsc[t][g];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Y[t][i] = fmaf(ds, acc[t][u][i], Y[t][i]);
+            for (int i = 0; i < 4; ++i) Y[t][i] = fmaf(ds, acc[t][u][i], Y[t][i]);
+          }
           cr[t] = fmaf(dg[g], xr[t][g], cr[t]);
         }
     }
-    float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * kRB;
+    float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * KS * kRB;
+    if constexpr (ONE) {
+      // lane block kb: term kb; the X correction once, in block 0
+      pw[kb * kRB + r16] = 2.f * Y[0][0] - (kb == 0 ? cr[0] : 0.f);
+    } else {
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const int mo = 4 * t + kb;
-      if (mo < M) pw[mo * kRB + r16] = 2.f * ((Y[t][0] + Y[t][1]) + (Y[t][2] + Y[t][3])) - cr[t];
+      for (int t = 0; t < TILES; ++t) {
+        const int mo = 4 * t + kb;
+        if (mo < M) pw[mo * kRB + r16] = 2.f * ((Y[t][0] + Y[t][1]) + (Y[t][2] + Y[t][3])) - cr[t];
+      }
     }
   };
 
@@ -636,7 +667,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     for (int i = 0; i < D; ++i)
       if (i < nrb) compute(wb[i], i);
     __syncthreads();
-    reduce_round(a, part, NW, RBR, M, rb0, nrb, 0, blockIdx.y);
+    reduce_round(a, part, NW, RBR, M, KS, rb0, nrb, 0, blockIdx.y);
     return;
   }
   for (int j0 = 0; j0 < nrb; j0 += D) {
@@ -647,7 +678,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
       issue(j + D, wb[i]);
       if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
         __syncthreads();
-        reduce_round(a, part, NW, RBR, M, rb0, nrb, j / RBR, blockIdx.y);
+        reduce_round(a, part, NW, RBR, M, KS, rb0, nrb, j / RBR, blockIdx.y);
       }
     }
   }
@@ -921,7 +952,7 @@ __global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs
       issue(j + D, wb[i]);
       if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
         __syncthreads();
-        reduce_round(a, part, NW, RBR, M, rb0, nrb, j / RBR, blockIdx.y);
+        reduce_round(a, part, NW, RBR, M, 1, rb0, nrb, j / RBR, blockIdx.y);
       }
     }
   }
