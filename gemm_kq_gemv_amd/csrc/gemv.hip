@@ -20,10 +20,13 @@
 //   of the same terms: sum (c-1) x' = 2 sum (c/2) x' - X (the Bonsai page,
 //   sec. 8.5, folds the -1 into an activation sum as well).  Each group of x'
 //   is scaled by its own power of two first, so its range suits e5m2.
-// * Q8_0.  Each int8 is converted to bf16 exactly and multiplied with x'
-//   split into bf16 hi + lo parts (2^-17 relative) by
-//   v_mfma_f32_16x16x32_bf16; one MFMA covers 16 weight rows x one 32-group
-//   for up to 8 activation rows.
+// * Q8_0, up to four activation rows.  The int8 weights go into
+//   v_mfma_i32_16x16x32_i8 as loaded; x' enters as four int8 digits of 7 bits
+//   under a power-of-two scale per row, the integer sums convert to fp32
+//   exactly, and one fma_mix per value applies the fp16 scale.  Five to eight
+//   rows: each int8 converts to bf16 exactly and x' is split into bf16 hi + lo
+//   parts (2^-17 relative), so that one v_mfma_f32_16x16x32_bf16 covers 16
+//   weight rows x one 32-group for all rows.
 // * Work split.  A workgroup owns a K-slice and a range of 16-row blocks.  Its
 //   waves split the K-slice (GS groups each) and hold their part of the
 //   activation operand in registers for the whole kernel.  Every wave
@@ -686,10 +689,22 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 
 // ---------------------------------------------------------------------------
 // Q8_0
+//
+// The int8 weights are the B operand of v_mfma_i32_16x16x32_i8 as loaded.  x'
+// is scaled per activation row (over the workgroup's K slice) by a power of two
+// 2^s that puts its largest magnitude in [32, 64), and written as four int8
+// digits: v = x' 2^s, q0 = rne(v), r0 = v - q0, q(t+1) = rne(128 rt),
+// r(t+1) = 128 rt - q(t+1).  Every digit lies in [-64, 64], and
+// x' 2^s = sum_t qt 2^(-7t) to within 2^-22, i.e. 2^-27 of the row's largest
+// magnitude.  Operand row 4t + m holds digit t of activation row m, so lane
+// block kb ends with digit kb of every row; each group's integer sum (below
+// 32*127*64 in magnitude) converts to fp32 exactly and is scaled by the group's
+// fp16 d with one fma_mix.  The digit weight 2^(-7kb) and 2^-s are applied once
+// per row block, and the four lane blocks' partials are added by the LDS
+// reduction in a fixed order.
 
 // GS groups of 32 per wave: 10 (16 waves at K=5120, at most 128 VGPRs) for
-// one activation row; 20 (8 waves, up to 256 VGPRs) for more, where the
-// staged rows and operands no longer fit the smaller register budget.
+// one activation row; 20 (8 waves, up to 256 VGPRs) for more.
 template <int GS_>
 struct Q8Cfg {
   static constexpr int GS = GS_;
@@ -698,11 +713,17 @@ struct Q8Cfg {
   static constexpr int MAXW = GS_ == 10 ? 16 : 8;
 };
 
-// LDS bytes: staged activations f32 [M][NW*GS*32], then the partials
-__host__ __device__ inline int q8_lds_part_offset(int M, int NW, int GS) { return M * NW * GS * 32 * 4; }
-__host__ __device__ inline int q8_lds_bytes(int M, int NW, int GS) {
-  return q8_lds_part_offset(M, NW, GS) + 2 * NW * 4 * M * kRB * 4;
+// LDS bytes: x' staged as fp32 [M][NW*GS*32] and rewritten in place as digits
+// (each 8-element chunk: [4 digits][8 bytes]), the slice maxima [M][NW], the
+// partials [2][NW][RBR][M][4 lane blocks][16] floats, then 16 zero bytes
+__host__ __device__ inline int q8_lds_max_offset(int M, int NW, int GS) { return M * NW * GS * 32 * 4; }
+__host__ __device__ inline int q8_lds_part_offset(int M, int NW, int GS) {
+  return q8_lds_max_offset(M, NW, GS) + (M * NW * 4 + 15) / 16 * 16;
 }
+__host__ __device__ inline int q8_lds_zero_offset(int M, int NW, int GS) {
+  return q8_lds_part_offset(M, NW, GS) + 2 * NW * 4 * M * 4 * kRB * 4;
+}
+__host__ __device__ inline int q8_lds_bytes(int M, int NW, int GS) { return q8_lds_zero_offset(M, NW, GS) + 16; }
 
 // rotation stages with h >= 16 in LDS: butterflies on E = 2^L values at stride 16
 template <int L>
@@ -743,8 +764,339 @@ __device__ void lds_stages(float* xs, int KRmax, int KR, int log2n, int M_) {
   }
 }
 
+// maximum over the 64 lanes of a wave, every lane receiving it (v >= 0: the
+// integer maximum of the bit patterns)
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));
+  u = max(max((uint32_t)__builtin_amdgcn_readlane((int)u, 0), (uint32_t)__builtin_amdgcn_readlane((int)u, 16)),
+          max((uint32_t)__builtin_amdgcn_readlane((int)u, 32), (uint32_t)__builtin_amdgcn_readlane((int)u, 48)));
+  return __uint_as_float(u);
+}
+
+// exponent s that puts bound * 2^s in [32, 64), within [-126, 126] so that 2^s and
+// 2^-s stay finite (0 for a zero, infinite or NaN bound)
+__device__ __forceinline__ int digit_exponent(float bound) {
+  const uint32_t ef = (__float_as_uint(bound) >> 23) & 0xFFu;
+  if (!(bound > 0.f) || ef == 0xFFu) return 0;
+  const int e = 5 - ((int)ef - 127);
+  return e < -126 ? -126 : (e > 126 ? 126 : e);
+}
+
+// low bytes of four words, in order, as one word
+__device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // [b0.0, b1.0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  // [b2.0, b3.0, 0, 0]
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);               // [lo.0, lo.1, hi.0, hi.1]
+}
+
 template <int M, bool DALIGN, int QGS>
 __global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
+  static_assert(M <= 4, "one operand tile: four digits of up to four activation rows");
+  constexpr int GS = Q8Cfg<QGS>::GS, D = Q8Cfg<QGS>::D, RBR = Q8Cfg<QGS>::RBR;
+  constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
+  constexpr int TILES = (M + 3) / 4;
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NW = blockDim.x >> 6;
+  const int r16 = lane & 15, kb = lane >> 4;
+
+  int g0, g1;
+  slice_groups(a, blockIdx.y, g0, g1);
+  const int KR = (g1 - g0) * 32;
+  const int64_t k0 = (int64_t)g0 * 32;
+  const int gw = wave * GS;  // relative to g0
+  const int vg = min(max(g1 - g0 - gw, 0), GS);
+  const int KRmax = NW * GS * 32;
+  float* xs = reinterpret_cast<float*>(lds);  // [M][KRmax]
+  float* rmax = reinterpret_cast<float*>(lds + q8_lds_max_offset(M, NW, GS));  // [M][NW]
+  float* part = reinterpret_cast<float*>(lds + q8_lds_part_offset(M, NW, GS));
+  uint8_t* zeros = lds + q8_lds_zero_offset(M, NW, GS);
+
+  const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
+  const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
+  const int nrb = rb1 - rb0;
+
+  // ---- activation loads first (rows past the first four after the weight
+  // loads, to bound the registers held)
+  constexpr int MPRE = M < 4 ? M : 4;
+  const int U16 = KR >> 4;  // 16-element units per activation row (<= threads)
+  const bool has_unit = tid < U16;
+  auto load_row = [&](int m, float (&v)[16]) {
+    if (has_unit) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + k0) + 4 * tid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = src[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.f;
+    }
+  };
+  float xv[MPRE][16];
+  uint4 sg = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int m = 0; m < MPRE; ++m) load_row(m, xv[m]);
+  if (has_unit && a.signs) sg = *reinterpret_cast<const uint4*>(a.signs + k0 + 16 * tid);
+
+  // ---- weight loads (pair q: groups 2q, 2q+1 of the wave)
+  uint32_t qoff[GS / 2];
+#pragma unroll
+  for (int q = 0; q < GS / 2; ++q) {
+    const int grp = 2 * q + (kb >> 1);
+    qoff[q] = grp < vg ? (uint32_t)(g0 + gw + grp) * 512u + 32u * r16 + 16u * (kb & 1) : kOutOfRange;
+  }
+  const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)(g0 + gw) * 2u;
+  struct WBuf {
+    uint4 q[GS / 2];
+    uint32_t d[DW];
+  };
+  const int64_t wrow0 = (int64_t)rb0 * kRB;
+  int64_t wrows = a.N - wrow0;
+  wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
+  // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
+  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
+  const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
+  auto issue = [&](int j, WBuf& b) {
+    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t dro = (j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows) + doff;
+#pragma unroll
+    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
+    if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
+#pragma unroll
+      for (int i = 0; i < DW / 4; ++i) {
+        const uint4 t = buffer_load_16B(rd, dro + 16u * i);
+        b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
+      }
+      if (DW % 4 >= 2) {
+        const uint2 t = buffer_load_8B(rd, dro + 16u * (DW / 4));
+        b.d[DW / 4 * 4] = t.x; b.d[DW / 4 * 4 + 1] = t.y;
+      }
+      if (DW % 2)
+        b.d[DW - 1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(dro + 4u * (DW - 1)), 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DW; ++i) {
+        const uint32_t lo = buffer_load_2B(rd, dro + 4u * i);
+        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, dro + 4u * i + 2u) : 0u;
+        b.d[i] = lo | (hi << 16);
+      }
+    }
+  };
+  WBuf wb[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue(i, wb[i]);
+
+  // ---- prologue: stage x (.) s in LDS, butterflies with stride < 16 in
+  // registers, wider ones in LDS
+  {
+    const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v[16];
+      if (m < MPRE) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = xv[m < MPRE ? m : 0][i];
+      } else {
+        load_row(m, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;  // int8 sign bit
+        v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (neg << 31));
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st < a.log2n) {
+          const int h = 1 << st;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if ((i & h) == 0) {
+              const float p0 = v[i], p1 = v[i + h];
+              v[i] = p0 + p1;
+              v[i + h] = p0 - p1;
+            }
+        }
+      }
+      if (has_unit) {
+        float4* dst = reinterpret_cast<float4*>(xs + m * KRmax) + 4 * tid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      }
+    }
+  }
+  __syncthreads();
+  if (a.log2n > 4) {
+    lds_stages(xs, KRmax, KR, a.log2n, M);
+    __syncthreads();
+  }
+
+  // ---- digits: the slice's largest |x'| per row, then every 8-element chunk
+  // of x' rewritten in place as its four digit planes
+  const int nch = KR >> 3;
+  {
+    float mx[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) mx[m] = 0.f;
+    for (int c = tid; c < nch; c += blockDim.x) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float4* src = reinterpret_cast<const float4*>(xs + m * KRmax + 8 * c);
+        const float4 f0 = src[0], f1 = src[1];
+        mx[m] = fmaxf(mx[m], fmaxf(fmaxf(fmaxf(fabsf(f0.x), fabsf(f0.y)), fmaxf(fabsf(f0.z), fabsf(f0.w))),
+                                   fmaxf(fmaxf(fabsf(f1.x), fabsf(f1.y)), fmaxf(fabsf(f1.z), fabsf(f1.w)))));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float w = wave_max_nonneg(mx[m]);
+      if (lane == 0) rmax[m * NW + wave] = w;
+    }
+    if (tid < 4) reinterpret_cast<uint32_t*>(zeros)[tid] = 0u;
+  }
+  __syncthreads();
+  float cs[M];   // inv_sqrt_n * 2^s: x' 2^s = staged value * cs
+  float ysc[M];  // 2^-s
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float r = 0.f;
+    for (int w = 0; w < NW; ++w) r = fmaxf(r, rmax[m * NW + w]);
+    const int e = digit_exponent(r * a.inv_sqrt_n);
+    cs[m] = ldexpf(a.inv_sqrt_n, e);
+    ysc[m] = ldexpf(1.f, -e);
+  }
+  {
+    // adding 1.5 * 2^23 rounds a float of magnitude below 2^22 to the nearest
+    // integer (ties to even) and leaves it, two's complement, in the low bits
+    const float kRound = 12582912.f;
+    for (int c = tid; c < nch; c += blockDim.x) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float4* ptr = reinterpret_cast<float4*>(xs + m * KRmax + 8 * c);
+        const float4 f0 = ptr[0], f1 = ptr[1];
+        float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        uint32_t dg[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint32_t bits[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float u = (t == 0 ? v[i] * cs[m] : v[i]) + kRound;
+            bits[i] = __float_as_uint(u);
+            if (t < 3) {
+              const float q = u - kRound;
+              v[i] = ((t == 0 ? v[i] * cs[m] : v[i]) - q) * 128.f;
+            }
+          }
+          dg[t][0] = low_bytes(bits[0], bits[1], bits[2], bits[3]);
+          dg[t][1] = low_bytes(bits[4], bits[5], bits[6], bits[7]);
+        }
+        ptr[0] = __builtin_bit_cast(float4, make_uint4(dg[0][0], dg[0][1], dg[1][0], dg[1][1]));
+        ptr[1] = __builtin_bit_cast(float4, make_uint4(dg[2][0], dg[2][1], dg[3][0], dg[3][1]));
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- operand: lane (r16, kb) holds digit r16 / 4 of activation row
+  // 4 * tile + r16 % 4 at the 8 positions that operand block kb covers (the
+  // weight operand's order: bytes {0, 16, 8, 24}[kb] + 0..7 of each group)
+  long aop[TILES][GS];
+  float pscale[TILES][4];  // 2^-s * 2^(-7 kb) of the lane's output rows
+  {
+    const int dt = r16 >> 2;
+    const int base = ((kb & 1) << 4) | ((kb & 2) << 2);  // {0, 16, 8, 24}[kb]
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int ma = 4 * t + (r16 & 3);
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const int pos = (gw + g) * 32 + base;
+        const uint8_t* src =
+            ma < M && g < vg ? reinterpret_cast<const uint8_t*>(xs + (ma < M ? ma : 0) * KRmax + pos) + 8 * dt : zeros;
+        aop[t][g] = *reinterpret_cast<const long*>(src);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pscale[t][i] = 4 * t + i < M ? ldexpf(ysc[4 * t + i < M ? 4 * t + i : 0], -7 * kb) : 0.f;
+    }
+  }
+
+  // ---- main loop over row blocks
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 izero = {0, 0, 0, 0};
+  auto compute = [&](const WBuf& b, int j) {
+    float Y[TILES][4];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Y[t][i] = 0.f;
+#pragma unroll
+    for (int q = 0; q < GS / 2; ++q) {
+      uint2 wq[2];
+      pair_to_operands(b.q[q], wq[0], wq[1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = 2 * q + h;
+        // groups past the slice have zero operands; their scale is some other
+        // finite one, or zero past the plane
+        const float dd = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+        const long bq = (long)(((uint64_t)wq[h].y << 32) | wq[h].x);
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          const i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[t][g], bq, izero, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * t + i < M) Y[t][i] = fmaf(dd, (float)acc[i], Y[t][i]);
+        }
+      }
+    }
+    float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * 4 * kRB;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * t + i < M) pw[((4 * t + i) * 4 + kb) * kRB + r16] = Y[t][i] * pscale[t][i];
+  };
+
+  for (int j0 = 0; j0 < nrb; j0 += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int j = j0 + i;
+      if (j < nrb) compute(wb[i], j);
+      issue(j + D, wb[i]);
+      if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
+        __syncthreads();
+        reduce_round(a, part, NW, RBR, M, 4, rb0, nrb, j / RBR, blockIdx.y);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0, five to eight activation rows: the int8 digits would need two operand
+// tiles (two MFMAs per group); here each int8 weight converts to bf16 exactly
+// and x enters as bf16 hi + lo parts (2^-17 relative), so one
+// v_mfma_f32_16x16x32_bf16 covers 16 weight rows x one 32-group for all 8
+// rows.  Lane (i, kb) of the operand holds activation row i/2 (hi part for
+// even i, lo for odd i).
+
+// LDS bytes: staged activations f32 [M][NW*GS*32], then the partials
+// [2][NW][RBR][M][16] floats
+__host__ __device__ inline int q8b_lds_part_offset(int M, int NW, int GS) { return M * NW * GS * 32 * 4; }
+__host__ __device__ inline int q8b_lds_bytes(int M, int NW, int GS) {
+  return q8b_lds_part_offset(M, NW, GS) + 2 * NW * 4 * M * kRB * 4;
+}
+
+template <int M, bool DALIGN, int QGS>
+__global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_bf16_kernel(GemvArgs a) {
   constexpr int GS = Q8Cfg<QGS>::GS, D = Q8Cfg<QGS>::D, RBR = Q8Cfg<QGS>::RBR;
   constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
   extern __shared__ __align__(16) uint8_t lds[];
@@ -763,7 +1115,7 @@ __global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs
   const int vg = min(max(g1 - g0 - gw, 0), GS);
   const int KRmax = NW * GS * 32;
   float* xs = reinterpret_cast<float*>(lds);  // [M][KRmax]
-  float* part = reinterpret_cast<float*>(lds + q8_lds_part_offset(M, NW, GS));
+  float* part = reinterpret_cast<float*>(lds + q8b_lds_part_offset(M, NW, GS));
 
   const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
   const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
@@ -993,7 +1345,8 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   };
   auto lds_for = [&](int S) {
     const int nw = waves_for(S);
-    return pq2 ? pq2_lds_bytes((int)M, nw, GS) : q8_lds_bytes((int)M, nw, GS);
+    return pq2 ? pq2_lds_bytes((int)M, nw, GS)
+               : (M <= 4 ? q8_lds_bytes((int)M, nw, GS) : q8b_lds_bytes((int)M, nw, GS));
   };
   auto fits = [&](int S) { return waves_for(S) <= MAXW && lds_for(S) <= kLdsBudget; };
   int S;
@@ -1058,8 +1411,12 @@ static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t s
   }
   constexpr int QGS = M == 1 ? 10 : 20;  // as plan_gemv chooses
   if (p.gs != QGS) return -1;
-  return p.dalign ? launch_kernel(gemv_q8_kernel<M, true, QGS>, a, p, st)
-                  : launch_kernel(gemv_q8_kernel<M, false, QGS>, a, p, st);
+  if constexpr (M <= 4)
+    return p.dalign ? launch_kernel(gemv_q8_kernel<M, true, QGS>, a, p, st)
+                    : launch_kernel(gemv_q8_kernel<M, false, QGS>, a, p, st);
+  else
+    return p.dalign ? launch_kernel(gemv_q8_bf16_kernel<M, true, QGS>, a, p, st)
+                    : launch_kernel(gemv_q8_bf16_kernel<M, false, QGS>, a, p, st);
 }
 
 int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,

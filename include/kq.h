@@ -141,6 +141,11 @@ size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N,
  * x' = x (.) s, no transform).  x is fp32 [M][K]; y is fp32 [M][N].
  * Arithmetic: x' in fp32, codes decoded exactly, fp32 accumulation; each
  * output is within 1e-3 * sum_k |deq(W)[n][k] x'[m][k]| of the exact value.
+ * Representation limits (outside them that bound can fail for an output whose
+ * weights touch only the small elements): PQ2_0 holds each x' element to
+ * 2^-12 of itself down to about 2^-30 of the largest |x'| in its 128-group;
+ * Q8_0 with M <= 4 holds each element to 2^-27 of the largest |x'| of its
+ * row within the K slice (M >= 5: 2^-17 of itself).
  * split_k: 1 = one pass over K; S > 1 splits K into S contiguous ranges of
  * whole blocks whose fp32 partial sums are added in ascending order
  * (deterministic, no atomics); 0 = chosen by the library.  Results are
