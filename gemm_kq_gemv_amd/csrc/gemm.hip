@@ -48,10 +48,11 @@ constexpr int FM = WM / 16, FN = WN / 16;            // 8 x 5 MFMA tiles per wav
 struct GemmArgs {
   const uint16_t* xb;   // x' bf16 [M][K]
   const uint8_t* qs;    // code plane (16-row tiles)
-  const uint16_t* dpl;  // scale plane [N][K/128]
+  const uint8_t* dpl;   // scale plane (16-row x 8-block chunks)
   float* y;             // [M][N]
   int64_t M, N, K;
   int64_t d_per_row;    // blocks per row (K / 128)
+  int64_t d_tile_bytes; // scale bytes per 16-row tile
   int mt, nt;           // tile counts
 };
 
@@ -116,10 +117,11 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   const BufRsrc ra_rs = make_rsrc(a.xb + m0 * a.K, (uint32_t)(arows * a.K * 2));
   // codes of row n0 + t: tile (n0 + t) / 16 (n0 is a multiple of 16), row t % 16
   const BufRsrc rq_rs = make_rsrc(a.qs + (n0 >> 4) * G * 512, (uint32_t)((brows + 15) / 16 * G * 512));
-  const BufRsrc rd_rs = make_rsrc(a.dpl + n0 * G, (uint32_t)(brows * G * 2));
+  // scales of row n0 + t, block b: chunk ((n0 + t) / 16, b / 8), row t % 16
+  const BufRsrc rd_rs = make_rsrc(a.dpl + (n0 >> 4) * a.d_tile_bytes, (uint32_t)((brows + 15) / 16 * a.d_tile_bytes));
   const uint32_t a_off = (uint32_t)(arow * a.K + achunk) * 2u;
   const uint32_t q_off = (uint32_t)((tid >> 4) * G * 512 + (tid & 15) * 32);
-  const uint32_t d_off = (uint32_t)(tid * G) * 2u;
+  const uint32_t d_off = (uint32_t)((tid >> 4) * a.d_tile_bytes + (tid & 15) * 16);
 
   // staging registers for two K-tiles: the tile stored during a K-tile's
   // multiplies was loaded one iteration earlier, so storing it never waits
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
     for (int i = 0; i < 8; ++i)
       ra[set][i] = buffer_load_16B(ra_rs, a_off + (uint32_t)((32 * i * a.K + k0) * 2));
     rq[set] = buffer_load_16B(rq_rs, q_off + (uint32_t)((k0 >> 7) * 512 + ((k0 & 127) >> 2)));
-    rd[set] = f16_bits_to_f32(buffer_load_2B(rd_rs, d_off + (uint32_t)(k0 >> 7) * 2u));
+    rd[set] = f16_bits_to_f32(buffer_load_2B(rd_rs, d_off + (uint32_t)((k0 >> 10) * 256 + ((k0 >> 7) & 7) * 2)));
   };
   auto sstore = [&](int buf, int set) {
     uint16_t* A = smem + buf * STAGE_ELEMS;
@@ -254,12 +256,13 @@ int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_b
   GemmArgs a;
   a.xb = xb;
   a.qs = pv.qs;
-  a.dpl = (const uint16_t*)pv.d;
+  a.dpl = pv.d;
   a.y = y;
   a.M = M;
   a.N = N;
   a.K = K;
   a.d_per_row = pv.d_per_row;
+  a.d_tile_bytes = pv.d_tile_bytes;
   a.mt = (int)((M + TM - 1) / TM);
   a.nt = (int)((N + TN - 1) / TN);
   // the kernel needs more than 64 KiB of dynamic LDS; set once (thread-safe

@@ -76,7 +76,7 @@ struct GemvArgs {
   float* out;            // y [M][N] (S == 1) or partials [S][M][N]
   int64_t N, K;
   uint32_t row_bytes;    // qs bytes per weight row (32 per group)
-  uint32_t d_row_bytes;  // scale bytes per weight row
+  uint32_t d_tile_bytes; // scale bytes per 16-row tile (256 per 8 groups)
   int G;                 // groups per row
   int U;                 // groups per rotation block (slices hold whole blocks)
   int S;                 // K slices
@@ -407,23 +407,23 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     const int grp = 2 * q + (kb >> 1);
     qoff[q] = grp < vg ? (uint32_t)(gw + grp) * 512u + 32u * r16 + 16u * (kb & 1) : kOutOfRange;
   }
-  const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)gw * 2u;
+  // scales of row r16, group gw: chunk gw / 8 of the tile, row r16, slot gw % 8
+  const uint32_t doff = (uint32_t)(gw >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gw & 7) * 2u;
   struct WBuf {
     uint4 q[GS / 2];
     uint32_t d[GS / 2];
   };
   const int64_t wrow0 = (int64_t)rb0 * kRB;
-  int64_t wrows = a.N - wrow0;
-  wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
-  const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
+  // scales: the workgroup's whole 16-row tiles of the scale plane (padding is zero)
+  const BufRsrc rd = make_rsrc(a.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t rod = j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows;
+    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
 #pragma unroll
     for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
-    if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
+    if (DALIGN) {  // gw % GS == 0: the GS scales are one aligned run of a chunk row
       if constexpr (GS == 4) {
         const uint2 t = buffer_load_8B(rd, doff + rod);
         b.d[0] = t.x; b.d[1] = t.y;
@@ -432,9 +432,15 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
         b.d[0] = t.x; b.d[1] = t.y; b.d[2] = t.z; b.d[3] = t.w;
       }
     } else {
+      // one scale per load, each at its own chunk and slot
 #pragma unroll
-      for (int i = 0; i < GS / 2; ++i)
-        b.d[i] = buffer_load_2B(rd, doff + rod + 4u * i) | (buffer_load_2B(rd, doff + rod + 4u * i + 2u) << 16);
+      for (int i = 0; i < GS / 2; ++i) {
+        const int ge = gw + 2 * i, go = ge + 1;
+        const uint32_t oe = (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u;
+        const uint32_t oo = (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u;
+        const uint32_t rbase = (uint32_t)r16 * 16u + rod;
+        b.d[i] = buffer_load_2B(rd, rbase + oe) | (buffer_load_2B(rd, rbase + oo) << 16);
+      }
     }
   };
   // Only the first row block is loaded before the prologue.  A wave stalls at a
@@ -589,8 +595,8 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     uint2 wq[GS];
 #pragma unroll
     for (int q = 0; q < GS / 2; ++q) pair_to_operands(b.q[q], wq[2 * q], wq[2 * q + 1]);
-    // groups past the slice (g >= vg) read some other finite scale, or zero
-    // past the plane; their 2^-e and X are zero, so they add nothing
+    // groups past the slice (g >= vg) read some other finite scale, or the
+    // zero padding; their 2^-e and X are zero, so they add nothing
     float dg[GS];
 #pragma unroll
     for (int g = 0; g < GS; ++g) dg[g] = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
@@ -703,14 +709,18 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 // per row block, and the four lane blocks' partials are added by the LDS
 // reduction in a fixed order.
 
-// GS groups of 32 per wave: 10 (16 waves at K=5120, at most 128 VGPRs) for
-// one activation row; 20 (8 waves, up to 256 VGPRs) for more.
-template <int GS_>
+// 16 groups of 32 per wave (two chunks of scales).  Row blocks of weight loads
+// in flight: two for one activation row, one for two to four (their digit
+// operands take the registers), two again for the bf16 kernel of five to
+// eight rows, whose waves may use 256 VGPRs (at most 8 waves).
+__host__ __device__ constexpr int q8_rbr(int M) { return M == 1 ? 4 : 2; }  // row blocks per reduction round
+__host__ __device__ constexpr int q8_maxw(int M) { return M <= 4 ? 12 : 8; }
+template <int M>
 struct Q8Cfg {
-  static constexpr int GS = GS_;
-  static constexpr int D = 2;
-  static constexpr int RBR = 4;
-  static constexpr int MAXW = GS_ == 10 ? 16 : 8;
+  static constexpr int GS = 16;
+  static constexpr int D = M == 1 || M > 4 ? 2 : 1;
+  static constexpr int RBR = q8_rbr(M);
+  static constexpr int MAXW = q8_maxw(M);
 };
 
 // LDS bytes: x' staged as fp32 [M][NW*GS*32] and rewritten in place as digits
@@ -721,7 +731,7 @@ __host__ __device__ inline int q8_lds_part_offset(int M, int NW, int GS) {
   return q8_lds_max_offset(M, NW, GS) + (M * NW * 4 + 15) / 16 * 16;
 }
 __host__ __device__ inline int q8_lds_zero_offset(int M, int NW, int GS) {
-  return q8_lds_part_offset(M, NW, GS) + 2 * NW * 4 * M * 4 * kRB * 4;
+  return q8_lds_part_offset(M, NW, GS) + 2 * NW * q8_rbr(M) * M * 4 * kRB * 4;
 }
 __host__ __device__ inline int q8_lds_bytes(int M, int NW, int GS) { return q8_lds_zero_offset(M, NW, GS) + 16; }
 
@@ -793,10 +803,10 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);               // [lo.0, lo.1, hi.0, hi.1]
 }
 
-template <int M, bool DALIGN, int QGS>
-__global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
+template <int M, bool DALIGN>
+__global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
   static_assert(M <= 4, "one operand tile: four digits of up to four activation rows");
-  constexpr int GS = Q8Cfg<QGS>::GS, D = Q8Cfg<QGS>::D, RBR = Q8Cfg<QGS>::RBR;
+  constexpr int GS = Q8Cfg<M>::GS, D = Q8Cfg<M>::D, RBR = Q8Cfg<M>::RBR;
   constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
   constexpr int TILES = (M + 3) / 4;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -854,46 +864,48 @@ __global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs
     const int grp = 2 * q + (kb >> 1);
     qoff[q] = grp < vg ? (uint32_t)(g0 + gw + grp) * 512u + 32u * r16 + 16u * (kb & 1) : kOutOfRange;
   }
-  const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)(g0 + gw) * 2u;
+  // scales of row r16, group gq = g0 + gw: chunk gq / 8 of the tile, row r16, slot gq % 8
+  const int gq = g0 + gw;
+  const uint32_t doff = (uint32_t)(gq >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gq & 7) * 2u;
   struct WBuf {
     uint4 q[GS / 2];
     uint32_t d[DW];
   };
   const int64_t wrow0 = (int64_t)rb0 * kRB;
-  int64_t wrows = a.N - wrow0;
-  wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
-  const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
+  const BufRsrc rd = make_rsrc(a.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t dro = (j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows) + doff;
+    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    const uint32_t dro = rod + doff;
 #pragma unroll
     for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
-    if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
+    if (DALIGN) {  // gq % 8 == 0: GS / 8 whole chunk rows of 8 scales
 #pragma unroll
-      for (int i = 0; i < DW / 4; ++i) {
-        const uint4 t = buffer_load_16B(rd, dro + 16u * i);
+      for (int i = 0; i < GS / 8; ++i) {
+        const uint4 t = buffer_load_16B(rd, dro + 256u * i);
         b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
       }
-      if (DW % 4 >= 2) {
-        const uint2 t = buffer_load_8B(rd, dro + 16u * (DW / 4));
-        b.d[DW / 4 * 4] = t.x; b.d[DW / 4 * 4 + 1] = t.y;
-      }
-      if (DW % 2)
-        b.d[DW - 1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(dro + 4u * (DW - 1)), 0, 0);
     } else {
+      // one scale per load, each at its own chunk and slot
 #pragma unroll
       for (int i = 0; i < DW; ++i) {
-        const uint32_t lo = buffer_load_2B(rd, dro + 4u * i);
-        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, dro + 4u * i + 2u) : 0u;
+        const int ge = gq + 2 * i, go = ge + 1;
+        const uint32_t rbase = (uint32_t)r16 * 16u + rod;
+        const uint32_t lo = buffer_load_2B(rd, rbase + (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u);
+        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, rbase + (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u) : 0u;
         b.d[i] = lo | (hi << 16);
       }
     }
   };
+  // One row: only the first row block is requested before the prologue (a
+  // wave stalls at a load it cannot issue while the memory pipeline is full,
+  // and a stalled wave does no arithmetic); the rest after it.
+  constexpr int DPRE = M == 1 ? 1 : D;
   WBuf wb[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) issue(i, wb[i]);
+  for (int i = 0; i < DPRE; ++i) issue(i, wb[i]);
 
   // ---- prologue: stage x (.) s in LDS, butterflies with stride < 16 in
   // registers, wider ones in LDS
@@ -1006,6 +1018,12 @@ __global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs
   }
   __syncthreads();
 
+  if constexpr (DPRE < D) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = DPRE; i < D; ++i) issue(i, wb[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // ---- operand: lane (r16, kb) holds digit r16 / 4 of activation row
   // 4 * tile + r16 % 4 at the 8 positions that operand block kb covers (the
   // weight operand's order: bytes {0, 16, 8, 24}[kb] + 0..7 of each group)
@@ -1092,12 +1110,12 @@ __global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_kernel(GemvArgs
 // [2][NW][RBR][M][16] floats
 __host__ __device__ inline int q8b_lds_part_offset(int M, int NW, int GS) { return M * NW * GS * 32 * 4; }
 __host__ __device__ inline int q8b_lds_bytes(int M, int NW, int GS) {
-  return q8b_lds_part_offset(M, NW, GS) + 2 * NW * 4 * M * kRB * 4;
+  return q8b_lds_part_offset(M, NW, GS) + 2 * NW * q8_rbr(M) * M * kRB * 4;
 }
 
-template <int M, bool DALIGN, int QGS>
-__global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_bf16_kernel(GemvArgs a) {
-  constexpr int GS = Q8Cfg<QGS>::GS, D = Q8Cfg<QGS>::D, RBR = Q8Cfg<QGS>::RBR;
+template <int M, bool DALIGN>
+__global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvArgs a) {
+  constexpr int GS = Q8Cfg<M>::GS, D = Q8Cfg<M>::D, RBR = Q8Cfg<M>::RBR;
   constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
   extern __shared__ __align__(16) uint8_t lds[];
 
@@ -1152,39 +1170,37 @@ __global__ __launch_bounds__(Q8Cfg<QGS>::MAXW * 64) void gemv_q8_bf16_kernel(Gem
     const int grp = 2 * q + (kb >> 1);
     qoff[q] = grp < vg ? (uint32_t)(g0 + gw + grp) * 512u + 32u * r16 + 16u * (kb & 1) : kOutOfRange;
   }
-  const uint32_t doff = (uint32_t)r16 * a.d_row_bytes + (uint32_t)(g0 + gw) * 2u;
+  // scales of row r16, group gq = g0 + gw: chunk gq / 8 of the tile, row r16, slot gq % 8
+  const int gq = g0 + gw;
+  const uint32_t doff = (uint32_t)(gq >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gq & 7) * 2u;
   struct WBuf {
     uint4 q[GS / 2];
     uint32_t d[DW];
   };
   const int64_t wrow0 = (int64_t)rb0 * kRB;
-  int64_t wrows = a.N - wrow0;
-  wrows = wrows < 0 ? 0 : (wrows > (int64_t)nrb * kRB ? (int64_t)nrb * kRB : wrows);
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
-  const BufRsrc rd = make_rsrc(a.dpl + wrow0 * a.d_row_bytes, (uint32_t)(wrows * a.d_row_bytes));
+  const BufRsrc rd = make_rsrc(a.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t dro = (j < nrb ? (uint32_t)j * (kRB * a.d_row_bytes) : kFarRows) + doff;
+    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    const uint32_t dro = rod + doff;
 #pragma unroll
     for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
-    if (DALIGN) {  // 2*GS scale bytes at a 4-byte aligned offset
+    if (DALIGN) {  // gq % 8 == 0: GS / 8 whole chunk rows of 8 scales
 #pragma unroll
-      for (int i = 0; i < DW / 4; ++i) {
-        const uint4 t = buffer_load_16B(rd, dro + 16u * i);
+      for (int i = 0; i < GS / 8; ++i) {
+        const uint4 t = buffer_load_16B(rd, dro + 256u * i);
         b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
       }
-      if (DW % 4 >= 2) {
-        const uint2 t = buffer_load_8B(rd, dro + 16u * (DW / 4));
-        b.d[DW / 4 * 4] = t.x; b.d[DW / 4 * 4 + 1] = t.y;
-      }
-      if (DW % 2)
-        b.d[DW - 1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(dro + 4u * (DW - 1)), 0, 0);
     } else {
+      // one scale per load, each at its own chunk and slot
 #pragma unroll
       for (int i = 0; i < DW; ++i) {
-        const uint32_t lo = buffer_load_2B(rd, dro + 4u * i);
-        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, dro + 4u * i + 2u) : 0u;
+        const int ge = gq + 2 * i, go = ge + 1;
+        const uint32_t rbase = (uint32_t)r16 * 16u + rod;
+        const uint32_t lo = buffer_load_2B(rd, rbase + (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u);
+        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, rbase + (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u) : 0u;
         b.d[i] = lo | (hi << 16);
       }
     }
@@ -1332,10 +1348,8 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   const int n = block_len > 1 ? block_len : 1;
   // PQ2_0: half-word lanes unless a rotation block needs a whole wave
   const int epl = pq2 ? (n <= 512 ? 8 : 16) : 0;
-  const int q8gs = M == 1 ? 10 : 20;
-  const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : q8gs;
-  const int MAXW = pq2 ? (epl == 8 ? Pq2Cfg<8>::MAXW : Pq2Cfg<16>::MAXW)
-                       : (q8gs == 10 ? Q8Cfg<10>::MAXW : Q8Cfg<20>::MAXW);
+  const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : Q8Cfg<1>::GS;
+  const int MAXW = pq2 ? (epl == 8 ? Pq2Cfg<8>::MAXW : Pq2Cfg<16>::MAXW) : q8_maxw((int)M);
   const int G = (int)(K / GROUP);
   const int U = n > GROUP ? n / GROUP : 1;
   const int NU = G / U;
@@ -1364,6 +1378,25 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   p.units = U;
   p.nw = waves_for(S);
   p.lds_bytes = lds_for(S);
+  // Slices in units of lcm(U, GS) groups start every wave on a multiple of
+  // GS, so that its scales are whole aligned runs; taken when that unit still
+  // allows S slices and they fit.
+  {
+    int ua = U;
+    while (ua % GS) ua += U;
+    const int NA = G % ua == 0 ? G / ua : 0;
+    if (ua != U && S <= NA) {
+      const int nwa = ((NA + S - 1) / S * ua + GS - 1) / GS;
+      const int ldsa = pq2 ? pq2_lds_bytes((int)M, nwa, GS)
+                           : (M <= 4 ? q8_lds_bytes((int)M, nwa, GS) : q8b_lds_bytes((int)M, nwa, GS));
+      if (nwa <= MAXW && ldsa <= kLdsBudget) {
+        p.units = ua;
+        p.nw = nwa;
+        p.lds_bytes = ldsa;
+      }
+    }
+  }
+  const int NUp = G / p.units;
   p.total_rb = (int)((N + kRB - 1) / kRB);
   const int target = kTargetWGs / S > 0 ? kTargetWGs / S : 1;
   p.grid_x = p.total_rb < target ? p.total_rb : target;
@@ -1374,10 +1407,10 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
     p.split = -1;
     return p;
   }
-  // scale runs of a wave start on a 4-byte boundary when every slice starts
-  // on an even group and rows hold an even number of groups
-  bool even = G % 2 == 0;
-  for (int s = 0; s < S && even; ++s) even = part_start(s, NU / S, NU % S) * U % 2 == 0;
+  // a wave's scales are whole aligned runs when every slice starts on a
+  // multiple of GS groups (waves then start on multiples of GS)
+  bool even = true;
+  for (int s = 0; s < S && even; ++s) even = part_start(s, NUp / S, NUp % S) * p.units % GS == 0;
   p.dalign = even;
   return p;
 }
@@ -1409,14 +1442,13 @@ static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t s
     return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 16>, a, p, st)
                     : launch_kernel(gemv_pq2_kernel<M, false, 16>, a, p, st);
   }
-  constexpr int QGS = M == 1 ? 10 : 20;  // as plan_gemv chooses
-  if (p.gs != QGS) return -1;
+  if (p.gs != Q8Cfg<M>::GS) return -1;
   if constexpr (M <= 4)
-    return p.dalign ? launch_kernel(gemv_q8_kernel<M, true, QGS>, a, p, st)
-                    : launch_kernel(gemv_q8_kernel<M, false, QGS>, a, p, st);
+    return p.dalign ? launch_kernel(gemv_q8_kernel<M, true>, a, p, st)
+                    : launch_kernel(gemv_q8_kernel<M, false>, a, p, st);
   else
-    return p.dalign ? launch_kernel(gemv_q8_bf16_kernel<M, true, QGS>, a, p, st)
-                    : launch_kernel(gemv_q8_bf16_kernel<M, false, QGS>, a, p, st);
+    return p.dalign ? launch_kernel(gemv_q8_bf16_kernel<M, true>, a, p, st)
+                    : launch_kernel(gemv_q8_bf16_kernel<M, false>, a, p, st);
 }
 
 int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,
@@ -1433,7 +1465,7 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
   a.N = N;
   a.K = K;
   a.row_bytes = (uint32_t)pv.row_bytes;
-  a.d_row_bytes = (uint32_t)(pv.d_per_row * 2);
+  a.d_tile_bytes = (uint32_t)pv.d_tile_bytes;
   a.G = (int)(K / (fmt == kFmtPQ2 ? 128 : 32));
   a.U = p.units;
   a.S = p.split;

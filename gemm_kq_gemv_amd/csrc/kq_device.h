@@ -83,6 +83,15 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 __host__ __device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t wr, int64_t nb) {
   return (((n >> 4) * nb + (wr >> 3)) << 7) + ((n & 15) << 3) + (wr & 7);
 }
+// Scale plane tiling: the fp16 scale of block b of row n lives in chunk
+// (n / 16, b / 8) -- 16 rows x 8 blocks, row n % 16 at byte 16 * (n % 16),
+// block b % 8 at byte 2 * (b % 8) within it -- and chunk (t, c) starts at
+// byte 256 * (t * C + c), C = ceil(nb / 8).  The 8 scales of a row within a
+// chunk are 16 contiguous bytes, and a 16-row block's scales for 8 blocks one
+// 256-byte run.  Index in 16-bit units:
+__host__ __device__ __forceinline__ int64_t tiled_scale(int64_t n, int64_t b, int64_t C) {
+  return (((n >> 4) * C + (b >> 3)) << 7) + ((n & 15) << 3) + (b & 7);
+}
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;  // an offset past any range used here
 __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,

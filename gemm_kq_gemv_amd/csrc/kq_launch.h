@@ -15,9 +15,11 @@ inline int group_of(int fmt) { return fmt == kFmtPQ2 ? 128 : 32; }
 struct PlanarView {
   uint8_t* qs;
   uint8_t* d;
-  int64_t qs_bytes;    // code plane: whole 16-row tiles, ceil(N/16)*16 * row_bytes
-  int64_t row_bytes;   // code bytes per row (32 per block)
-  int64_t d_per_row;   // scales per row
+  int64_t qs_bytes;      // code plane: whole 16-row tiles, ceil(N/16)*16 * row_bytes
+  int64_t row_bytes;     // code bytes per row (32 per block)
+  int64_t d_per_row;     // scales per row (blocks)
+  int64_t d_chunks;      // scale chunks of 8 blocks per 16-row tile, ceil(d_per_row / 8)
+  int64_t d_tile_bytes;  // scale bytes per 16-row tile, 256 * d_chunks
   int64_t total_bytes;
 };
 
@@ -27,7 +29,9 @@ inline PlanarView planar_view(int fmt, int64_t N, int64_t K, void* base) {
   v.qs_bytes = (N + 15) / 16 * 16 * v.row_bytes;
   int64_t d_off = (v.qs_bytes + 255) / 256 * 256;
   v.d_per_row = K / group_of(fmt);
-  v.total_bytes = d_off + N * v.d_per_row * 2;
+  v.d_chunks = (v.d_per_row + 7) / 8;
+  v.d_tile_bytes = 256 * v.d_chunks;
+  v.total_bytes = d_off + (N + 15) / 16 * v.d_tile_bytes;
   v.qs = (uint8_t*)base;
   v.d = (uint8_t*)base + d_off;
   return v;

@@ -14,11 +14,23 @@
 // threads cover one 32-group.  The group max is reduced across those 8 lanes
 // with xor shuffles, so one pass reads W once with coalesced 64/16-byte loads;
 // each group's 8 words land as 32 contiguous bytes of its tile, and padding
-// rows are written as zeros.
+// rows are written as zeros.  The group's first thread writes its scale into
+// the tiled scale plane (zero for padding rows); the thread of a row's last
+// block also zeroes the unused block slots of that row's last chunk.
 #include "kq_device.h"
 #include "kq_launch.h"
 
 namespace kq {
+
+// scale of the group whose first code word is g (words_per_row = 8 nb); the
+// last block of a row also clears the padding slots of its chunk
+__device__ __forceinline__ void store_scale(uint16_t* dplane, int64_t g, int64_t words_per_row, int64_t C,
+                                            uint16_t d16) {
+  const int64_t n = g / words_per_row, b = (g % words_per_row) >> 3, nb = words_per_row >> 3;
+  dplane[tiled_scale(n, b, C)] = d16;
+  if (b == nb - 1)
+    for (int64_t p = nb; p < 8 * C; ++p) dplane[tiled_scale(n, p, C)] = 0;
+}
 
 __device__ __forceinline__ float group8_max(float a) {
   // the 8 lanes of a group are aligned to 8 within the wave
@@ -30,7 +42,7 @@ __device__ __forceinline__ float group8_max(float a) {
 
 __global__ __launch_bounds__(256) void pack_pq2_kernel(
     const float* __restrict__ W, uint32_t* __restrict__ qs, uint16_t* __restrict__ dplane,
-    int64_t n_words, int64_t live_words, int64_t words_per_row) {
+    int64_t n_words, int64_t live_words, int64_t words_per_row, int64_t C) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool in_plane = g < n_words;
   bool live = g < live_words;
@@ -64,13 +76,13 @@ __global__ __launch_bounds__(256) void pack_pq2_kernel(
   }
   if (in_plane) {
     qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? word : 0u;
-    if (live && (g & 7) == 0) dplane[g >> 3] = d16;
+    if ((g & 7) == 0) store_scale(dplane, g, words_per_row, C, live ? d16 : (uint16_t)0);
   }
 }
 
 __global__ __launch_bounds__(256) void pack_q8_kernel(
     const float* __restrict__ W, uint32_t* __restrict__ qs, uint16_t* __restrict__ dplane,
-    int64_t n_words, int64_t live_words, int64_t words_per_row) {
+    int64_t n_words, int64_t live_words, int64_t words_per_row, int64_t C) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool in_plane = g < n_words;
   bool live = g < live_words;
@@ -93,18 +105,18 @@ __global__ __launch_bounds__(256) void pack_q8_kernel(
   }
   if (in_plane) {
     qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? word : 0u;
-    if (live && (g & 7) == 0) dplane[g >> 3] = d16;
+    if ((g & 7) == 0) store_scale(dplane, g, words_per_row, C, live ? d16 : (uint16_t)0);
   }
 }
 
 // Dequantize: one thread per 32-bit code word of the N real rows (row-major).
 __global__ __launch_bounds__(256) void unpack_pq2_kernel(
     const uint32_t* __restrict__ qs, const uint16_t* __restrict__ dplane,
-    float* __restrict__ W, int64_t n_words, int64_t words_per_row) {
+    float* __restrict__ W, int64_t n_words, int64_t words_per_row, int64_t C) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_words) return;
   uint32_t word = qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)];
-  float d = f16_bits_to_f32(dplane[g >> 3]);
+  float d = f16_bits_to_f32(dplane[tiled_scale(g / words_per_row, (g % words_per_row) >> 3, C)]);
   float4* dst = reinterpret_cast<float4*>(W) + g * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -117,11 +129,11 @@ __global__ __launch_bounds__(256) void unpack_pq2_kernel(
 
 __global__ __launch_bounds__(256) void unpack_q8_kernel(
     const uint32_t* __restrict__ qs, const uint16_t* __restrict__ dplane,
-    float* __restrict__ W, int64_t n_words, int64_t words_per_row) {
+    float* __restrict__ W, int64_t n_words, int64_t words_per_row, int64_t C) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_words) return;
   uint32_t word = qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)];
-  float d = f16_bits_to_f32(dplane[g >> 3]);
+  float d = f16_bits_to_f32(dplane[tiled_scale(g / words_per_row, (g % words_per_row) >> 3, C)]);
   float v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) v[j] = d * (float)(int8_t)(word >> (8 * j));
@@ -136,9 +148,9 @@ int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed,
   const int64_t n_words = pv.qs_bytes / 4, wpr = pv.row_bytes / 4, live = N * wpr;
   if (n_words == 0) return 0;
   if (fmt == 1)
-    pack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr);
+    pack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr, pv.d_chunks);
   else
-    pack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr);
+    pack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr, pv.d_chunks);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -148,9 +160,9 @@ int launch_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W,
   const int64_t wpr = pv.row_bytes / 4, n_words = N * wpr;
   if (n_words == 0) return 0;
   if (fmt == 1)
-    unpack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words, wpr);
+    unpack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words, wpr, pv.d_chunks);
   else
-    unpack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words, wpr);
+    unpack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)pv.qs, (const uint16_t*)pv.d, W, n_words, wpr, pv.d_chunks);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

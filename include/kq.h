@@ -41,12 +41,18 @@
  *                block holding element 16*i + j at bits 2*j ([BT] 3.1
  *                "Word view"); for Q8_0 they are the 32 int8 codes.
  *     d plane  : at byte offset round_up(qs plane size, 256): one IEEE
- *                binary16 scale per block, [N][nb], row-major, little
- *                endian.
+ *                binary16 scale per block (little endian), in chunks of
+ *                16 rows x 8 blocks: the scale of block b of row n sits in
+ *                chunk (n / 16, b / 8), which starts at byte
+ *                256 * ((n / 16) * C + b / 8), C = ceil(nb / 8), at byte
+ *                16 * (n % 16) + 2 * (b % 8) within it.  Slots of rows past N
+ *                and of blocks past nb are zero.  Plane size:
+ *                ceil(N/16) * C * 256 bytes.
  *   This is a lossless re-arrangement of the GGUF-style array of 34-byte
- *   blocks { fp16 d; uint8 qs[32] }: the scales move out and the code
- *   blocks of 16 rows are interleaved, so that a wave's 16 rows x 2 blocks
- *   are one contiguous KiB.
+ *   blocks { fp16 d; uint8 qs[32] }: the scales move out, the code blocks of
+ *   16 rows are interleaved so that a wave's 16 rows x 2 blocks are one
+ *   contiguous KiB, and a row's scales for 8 consecutive blocks are 16
+ *   contiguous bytes next to those of the other 15 rows of its tile.
  * Alignment.  All pointers must be 16-byte aligned, else KQ_EALIGN.
  * Errors.  Arguments are validated before anything is enqueued; on any
  *   error nothing is launched and no output byte is written.  A failed

@@ -201,15 +201,20 @@ int64_t kqo_planar_bytes(int fmt, int64_t N, int64_t K)
     int g = fmt_group(fmt);
     if (!g || N < 0 || K <= 0 || K % g) return -1;
     int64_t nb = K / g;
-    int64_t qs_bytes = (N + 15) / 16 * 16 * nb * 32;   /* whole 16-row tiles */
+    int64_t tiles = (N + 15) / 16;                      /* 16-row tiles */
+    int64_t qs_bytes = tiles * 16 * nb * 32;
     int64_t d_off = (qs_bytes + 255) / 256 * 256;
-    return d_off + N * nb * 2;
+    int64_t chunks = (nb + 7) / 8;                      /* 8 scales per chunk row */
+    return d_off + tiles * chunks * 256;
 }
 
 /* The 32 code bytes of block b of row n go to tile (n / 16, b): 16 rows x
  * 32 bytes, row n % 16 at byte 32 * (n % 16), tile (t, b) at byte
  * 512 * (t * nb + b).  Rows past N in the last tile stay zero.  The fp16
- * scales follow at the first 256-byte boundary, [N][nb] row-major. */
+ * scales follow at the first 256-byte boundary, in chunks of 16 rows x 8
+ * blocks: the scale of block b of row n sits in chunk (n / 16, b / 8), which
+ * starts at 256 * ((n / 16) * ceil(nb / 8) + b / 8), at byte
+ * 16 * (n % 16) + 2 * (b % 8) of it.  Slots past N or nb stay zero. */
 int kqo_aos_to_planar(int fmt, const uint8_t *aos, int64_t N, int64_t K,
                       uint8_t *planar)
 {
@@ -218,14 +223,16 @@ int kqo_aos_to_planar(int fmt, const uint8_t *aos, int64_t N, int64_t K,
     int64_t nb = K / g;
     int64_t qs_bytes = (N + 15) / 16 * 16 * nb * 32;
     int64_t d_off = (qs_bytes + 255) / 256 * 256;
+    int64_t chunks = (nb + 7) / 8;
     int64_t total = kqo_planar_bytes(fmt, N, K);
     memset(planar, 0, (size_t)total);
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < nb; ++b) {
             const uint8_t *blk = aos + (n * nb + b) * 34;
             memcpy(planar + ((n / 16) * nb + b) * 512 + (n % 16) * 32, blk + 2, 32);
-            planar[d_off + (n * nb + b) * 2 + 0] = blk[0];
-            planar[d_off + (n * nb + b) * 2 + 1] = blk[1];
+            int64_t at = d_off + ((n / 16) * chunks + b / 8) * 256 + (n % 16) * 16 + (b % 8) * 2;
+            planar[at + 0] = blk[0];
+            planar[at + 1] = blk[1];
         }
     }
     return 0;

@@ -65,8 +65,10 @@ int kqo_pack_q8_aos(const float *W, int64_t N, int64_t K, uint8_t *aos);
  * the 32 code bytes of each block, grouped in tiles of 16 rows x one block
  * (512 bytes; row r of the tile at byte 32*r), tiles ordered by 16-row block
  * and then by block along K, the last tile zero-padded past row N; then, at
- * the first 256-byte boundary after them, the fp16 scales row-major
- * ([N][K/128] or [N][K/32]).  [BT 3.1 "Word view"]: the code bytes of a
+ * the first 256-byte boundary after them, the fp16 scales in chunks of 16
+ * rows x 8 blocks (256 bytes; row r at byte 16*r, block b%8 at 2*(b%8)),
+ * chunks ordered by 16-row block and then by 8-block run along K, slots past
+ * N or past the row's blocks zero.  [BT 3.1 "Word view"]: the code bytes of a
  * block are a reinterpretation of its qs bytes; only their place moves.
  * fmt: 1 = PQ2_0, 2 = Q8_0. */
 int64_t kqo_planar_bytes(int fmt, int64_t N, int64_t K);

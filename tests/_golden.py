@@ -56,3 +56,19 @@ def d_offset(N: int, K: int, fmt: int) -> int:
     nb = K // (128 if fmt == 1 else 32)
     qs = (N + 15) // 16 * 16 * nb * 32
     return (qs + 255) // 256 * 256
+
+
+def scale_bytes(plane, N: int, K: int, fmt: int):
+    """Scale bytes [N][blocks][2] (little-endian fp16) from a packed buffer:
+    the scale plane holds chunks of 16 rows x 8 blocks (256 bytes, row r at
+    byte 16 r, block b % 8 at byte 2 (b % 8)), ordered by 16-row block and
+    then by 8-block run along K.  Also returns the padding slots (rows past N,
+    blocks past the row's last) as a flat array, which must be zero."""
+    import numpy as np
+    nb = K // (128 if fmt == 1 else 32)
+    nt, nc = (N + 15) // 16, (nb + 7) // 8
+    off = d_offset(N, K, fmt)
+    chunks = np.asarray(plane)[off:off + nt * nc * 256].reshape(nt, nc, 16, 8, 2)
+    full = chunks.transpose(0, 2, 1, 3, 4).reshape(nt * 16, nc * 8, 2)
+    pad = np.concatenate([full[N:].reshape(-1), full[:N, nb:].reshape(-1)])
+    return full[:N, :nb], pad

@@ -82,20 +82,22 @@ def test_pack_golden_fixtures():
     packed = kq.pack(1, dev(W))
     got = host(packed)
     rows = G.code_rows(got, 4, 128, 1)
-    d0 = G.d_offset(4, 128, 1)
+    sc, pad = G.scale_bytes(got, 4, 128, 1)
+    assert not pad.any()
     for i, c in enumerate("ABCD"):
         assert np.array_equal(rows[i], G.hex_bytes(g[f"block{c}_qs"])), c
-        d = int(got[d0 + 2 * i]) | (int(got[d0 + 2 * i + 1]) << 8)
+        d = int(sc[i, 0, 0]) | (int(sc[i, 0, 1]) << 8)
         assert d == int(g[f"block{c}_d16"], 16), c
     g8 = G.load("q8_quantize_block.txt")
     W8 = np.stack([G.sparse_block(g8["w"], 32), G.sparse_block(g8["b2_w"], 32)])
     got8 = host(kq.pack(2, dev(W8)))
     rows8 = G.code_rows(got8, 2, 32, 2)
-    d8 = G.d_offset(2, 32, 2)
+    sc8, pad8 = G.scale_bytes(got8, 2, 32, 2)
+    assert not pad8.any()
     assert np.array_equal(rows8[0].view(np.int8).astype(np.int64), G.ints(g8["q"]))
     assert np.array_equal(rows8[1].view(np.int8).astype(np.int64), G.ints(g8["b2_q"]))
-    assert int(got8[d8]) | (int(got8[d8 + 1]) << 8) == int(g8["d16"], 16)
-    assert int(got8[d8 + 2]) | (int(got8[d8 + 3]) << 8) == int(g8["b2_d16"], 16)
+    assert int(sc8[0, 0, 0]) | (int(sc8[0, 0, 1]) << 8) == int(g8["d16"], 16)
+    assert int(sc8[1, 0, 0]) | (int(sc8[1, 0, 1]) << 8) == int(g8["b2_d16"], 16)
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
@@ -122,7 +124,9 @@ def test_pack_unpack_roundtrip_c2_shape():
     packed = kq.pack(1, dev(W))
     Wd = host(kq.unpack(1, packed, N, K))
     # quantizer invariant: nearest ternary level, |w - deq| <= d/2
-    dpl = host(packed)[N * K // 4:].view("<f2").astype(np.float32).reshape(N, K // 128)
+    sc, pad = G.scale_bytes(host(packed), N, K, 1)
+    assert not pad.any()
+    dpl = np.ascontiguousarray(sc).view("<f2").astype(np.float32).reshape(N, K // 128)
     dF = np.repeat(dpl, 128, axis=1)
     assert np.all(np.abs(W - Wd) <= 0.5 * dF * (1 + 2 ** -20))
     # and repacking the dequantized weights reproduces the bytes

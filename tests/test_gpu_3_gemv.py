@@ -91,6 +91,7 @@ def test_c3_pq2_lm_head_full_size_sampled(split_k, c3_inputs):
     want = oracle.aos_to_planar(1, oracle.pack_pq2_aos(W[rows]), len(rows), K)
     got = host(packed)
     assert np.array_equal(G.code_rows(got, N, K, 1)[rows], G.code_rows(want, len(rows), K, 1))
+    assert np.array_equal(G.scale_bytes(got, N, K, 1)[0][rows], G.scale_bytes(want, len(rows), K, 1)[0])
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])

@@ -162,18 +162,22 @@ def test_pq2_aos_to_planar_layout():
     # past N zero
     qs_bytes = 16 * 2 * 32
     d_off = (qs_bytes + 255) // 256 * 256
-    assert pl.size == d_off + N * (K // 128) * 2
+    # scales: one chunk of 16 rows x 8 blocks (256 bytes), row n at 16 n,
+    # block b at 2 b; slots past N or past the 2 blocks zero
+    assert pl.size == d_off + 256
     tiles = pl[:qs_bytes].reshape(2, 16, 32)
     for n in range(N):
         for b in range(2):
             assert np.array_equal(tiles[b, n], aos[n, b, 2:])
     assert not tiles[:, N:].any()
-    assert np.array_equal(pl[d_off:].reshape(N, K // 128, 2), aos[:, :, :2])
+    chunk = pl[d_off:].reshape(16, 8, 2)
+    assert np.array_equal(chunk[:N, :2], aos[:, :, :2])
+    assert not chunk[N:].any() and not chunk[:, 2:].any()
     # word view of a row's code bytes: element 16i + j at bits 2j of LE word i
     row_codes = np.ascontiguousarray(tiles[:, :N].transpose(1, 0, 2)).reshape(N, K // 4)
     words = row_codes.view("<u4").reshape(N, K // 16)
     codes = np.stack([(words >> (2 * j)) & 3 for j in range(16)], axis=-1).reshape(N, K)
-    dF = pl[d_off:].view("<f2").astype(np.float64).reshape(N, K // 128)
+    dF = np.ascontiguousarray(chunk[:N, :2]).view("<f2").astype(np.float64).reshape(N, K // 128)
     deq = (codes.astype(np.float64) - 1) * np.repeat(dF, 128, axis=1)
     assert np.array_equal(deq, oracle.unpack_pq2_aos(aos.reshape(-1), N, K))
 
@@ -228,7 +232,10 @@ def test_q8_zero_block_and_planar():
     tiles = pl[:d_off].reshape(2, 16, 32)
     assert np.array_equal(tiles[:, :N].transpose(1, 0, 2), aos[:, :, 2:])
     assert not tiles[:, N:].any()
-    assert np.array_equal(pl[d_off:].reshape(N, 2, 2), aos[:, :, :2])
+    chunk = pl[d_off:].reshape(16, 8, 2)            # one 256-byte scale chunk
+    assert pl.size == d_off + 256
+    assert np.array_equal(chunk[:N, :2], aos[:, :, :2])
+    assert not chunk[N:].any() and not chunk[:, 2:].any()
 
 
 # --------------------------------------------------------------------------
