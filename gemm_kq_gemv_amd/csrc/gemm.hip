@@ -11,23 +11,27 @@
 // * Block tile 256 (tokens) x 160 (weight rows) x 64 (K), 4 waves in a 2 x 2
 //   arrangement; each wave owns 128 x 80 outputs = 8 x 5 accumulators of
 //   v_mfma_f32_16x16x32_bf16 (160 fp32 registers).  At M = 2048, N = 10240
-//   that is 512 tiles, two per CU, with no tail imbalance; the 128 x 80 wave
-//   tile reads 208 operand rows from LDS per 10240 outputs, which keeps LDS
-//   traffic under the MFMA time.
-// * x' (bf16, from the rotation pre-pass) and the dequantized weight tile are
-//   staged in LDS, double-buffered, rows padded to 72 bf16 so the 16-byte
-//   operand reads of 16 rows are bank-conflict free.  The next K-tile is
-//   fetched into registers while the current one is multiplied; one barrier
-//   per K-tile.
-// * Dequantization: 160 threads each expand the 64 codes of one weight row
-//   per K-tile: fp4 conversion of the nibble-spread codes gives c exactly,
-//   c*d - d is exact in fp32, and v_cvt_pk_bf16_f32 rounds pairs to bf16
-//   (nearest even) -- the same value as (q-1) * bf16(d).
+//   that is 512 tiles, two per CU, with no tail imbalance.
+// * Two LDS stages of x' (bf16) and the dequantized weight tile, 128-byte
+//   rows with the 16-byte chunks XOR-swizzled by (row / 2) % 8, so that the
+//   16-byte operand reads of 16 rows and the row-contiguous writes are both
+//   bank-conflict free without padding (2 x 52 KiB).  With the 72-element
+//   padded rows used before, a quarter of the LDS cycles were bank
+//   conflicts (SQ_LDS_BANK_CONFLICT).
+// * Software pipeline, one barrier per K-tile.  The MFMAs always run from
+//   registers: while the 40 MFMAs of k-step 0 of tile t run, the operands of
+//   its k-step 1 are read, tile t + 1 is dequantized and written to the
+//   other stage and tile t + 2 is fetched into the staging registers; after
+//   the barrier, the 40 MFMAs of k-step 1 overlap the reads of tile t + 1's
+//   k-step 0.  The stage written in the first half was last read before the
+//   previous barrier.
+// * Dequantization: the 160 x 64 codes of a tile are 1280 units of 8 codes,
+//   five per thread: fp4 conversion of the nibble-spread codes gives c
+//   exactly, c*d - d is exact in fp32, and v_cvt_pk_bf16_f32 rounds pairs to
+//   bf16 (nearest even) -- the same value as (q-1) * bf16(d).
 // * Tile order is XCD-aware: the 8 XCDs each take a contiguous eighth of the
 //   token tiles and walk every weight tile over it, so the x' rows stay in
 //   that XCD's L2 while the (ten times smaller) weight tiles stream past.
-//   Ordered the other way round, every XCD streamed all of x' once per
-//   weight tile it owned.
 #include <type_traits>
 
 #include "kq_device.h"
@@ -38,12 +42,16 @@ namespace kq {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int TM = 256, TN = 160, TK = 64;
-constexpr int LDK = TK + 8;  // padded row stride (bf16 elements)
-constexpr int TNS = 256;  // B rows staged per stage (rows past TN are padding, never read)
-constexpr int STAGE_ELEMS = (TM + TNS) * LDK;
-constexpr int GEMM_LDS_BYTES = 2 * STAGE_ELEMS * 2;  // 2 stages x (A + B) x bf16
-constexpr int WM = TM / 2, WN = TN / 2;              // wave tile 128 x 80
-constexpr int FM = WM / 16, FN = WN / 16;            // 8 x 5 MFMA tiles per wave
+constexpr int ROWB = TK * 2;                        // bytes per LDS row (no padding)
+constexpr int A_BYTES = TM * ROWB;                  // 32 KiB
+constexpr int B_BYTES = TN * ROWB;                  // 20 KiB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;      // 52 KiB
+constexpr int NSTAGE = 2;
+constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
+constexpr int WM = TM / 2, WN = TN / 2;             // wave tile 128 x 80
+constexpr int FM = WM / 16, FN = WN / 16;           // 8 x 5 MFMA tiles per wave
+constexpr int UNITS = TN * TK / 8 / 256;            // 8-code units per thread per tile (5)
+static_assert(TN * TK / 8 == UNITS * 256, "units must divide evenly");
 
 struct GemmArgs {
   const uint16_t* xb;   // x' bf16 [M][K]
@@ -56,27 +64,30 @@ struct GemmArgs {
   int mt, nt;           // tile counts
 };
 
-__device__ __forceinline__ void dequant_word_bf16(uint32_t w, float d, uint32_t* out8) {
-  // 16 codes -> 16 bf16 values (q-1)*d, packed in 8 dwords (element order)
-  const uint32_t e = w & 0x33333333u;
-  const uint32_t o = (w >> 2) & 0x33333333u;
-  float v[16];
-  f32x2 t;
-  t = codes2<0>(e); v[0] = t.x; v[2] = t.y;
-  t = codes2<0>(o); v[1] = t.x; v[3] = t.y;
-  t = codes2<1>(e); v[4] = t.x; v[6] = t.y;
-  t = codes2<1>(o); v[5] = t.x; v[7] = t.y;
-  t = codes2<2>(e); v[8] = t.x; v[10] = t.y;
-  t = codes2<2>(o); v[9] = t.x; v[11] = t.y;
-  t = codes2<3>(e); v[12] = t.x; v[14] = t.y;
-  t = codes2<3>(o); v[13] = t.x; v[15] = t.y;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    out8[i] = pack_bf16x2(fmaf(v[2 * i], d, -d), fmaf(v[2 * i + 1], d, -d));
+// 8 codes (16 bits, code j at bits 2j) -> 8 bf16 values (q-1)*d, as 4 dwords
+// in element order
+__device__ __forceinline__ uint4 dequant8_bf16(uint32_t h, float d) {
+  const uint32_t e = h & 0x3333u;         // codes 0, 2, 4, 6 in nibbles 0..3
+  const uint32_t o = (h >> 2) & 0x3333u;  // codes 1, 3, 5, 7
+  const f32x2 e0 = codes2<0>(e), e1 = codes2<1>(e), o0 = codes2<0>(o), o1 = codes2<1>(o);
+  return make_uint4(pack_bf16x2(fmaf(e0.x, d, -d), fmaf(o0.x, d, -d)),
+                    pack_bf16x2(fmaf(e0.y, d, -d), fmaf(o0.y, d, -d)),
+                    pack_bf16x2(fmaf(e1.x, d, -d), fmaf(o1.x, d, -d)),
+                    pack_bf16x2(fmaf(e1.y, d, -d), fmaf(o1.y, d, -d)));
+}
+
+// buffer loads with a per-thread offset and a uniform (scalar) one
+__device__ __forceinline__ uint4 load16_s(BufRsrc r, uint32_t voff, uint32_t soff) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load2_s(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 
 __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
-  extern __shared__ uint16_t smem[];
+  extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -104,53 +115,57 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   const int64_t m0 = (int64_t)m_tile * TM, n0 = (int64_t)n_tile * TN;
 
   // ---- global load geometry.  x' tile: load i of thread t covers row
-  // 32 i + t / 8, bytes 16 (t % 8) .. +15 of its 128-byte K-tile slice, so
-  // one instruction reads 8 whole rows.  Weights: thread t < TN expands the
-  // 64 codes of row n0 + t.
-  // All three go through buffer resources that cover exactly the block's
-  // valid rows, so rows past M or N (and staging rows past TN) read zeros
-  // with no branch: code 0 with scale 0 dequantizes to 0.
-  const int arow = tid >> 3, achunk = (tid & 7) * 8;  // row in a group of 32, bf16 offset
+  // 32 i + t / 8, bytes 16 (t % 8) .. +15 of its 128-byte K-tile slice.
+  // Weights: unit i of thread t is weight row 32 i + t / 8, codes
+  // 8 (t % 8) .. +7 of the K-tile (16 bits), with its block's scale.
+  // All go through buffer resources that cover exactly the block's valid
+  // rows, so rows past M or N read zeros with no branch: code 0 with scale 0
+  // dequantizes to 0.
+  const int arow = tid >> 3, achunk = tid & 7;
   const int64_t G = a.d_per_row;
   const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
   const int64_t brows = a.N - n0 < TN ? a.N - n0 : TN;
   const BufRsrc ra_rs = make_rsrc(a.xb + m0 * a.K, (uint32_t)(arows * a.K * 2));
-  // codes of row n0 + t: tile (n0 + t) / 16 (n0 is a multiple of 16), row t % 16
   const BufRsrc rq_rs = make_rsrc(a.qs + (n0 >> 4) * G * 512, (uint32_t)((brows + 15) / 16 * G * 512));
-  // scales of row n0 + t, block b: chunk ((n0 + t) / 16, b / 8), row t % 16
   const BufRsrc rd_rs = make_rsrc(a.dpl + (n0 >> 4) * a.d_tile_bytes, (uint32_t)((brows + 15) / 16 * a.d_tile_bytes));
-  const uint32_t a_off = (uint32_t)(arow * a.K + achunk) * 2u;
-  const uint32_t q_off = (uint32_t)((tid >> 4) * G * 512 + (tid & 15) * 32);
-  const uint32_t d_off = (uint32_t)((tid >> 4) * a.d_tile_bytes + (tid & 15) * 16);
+  const uint32_t a_off = (uint32_t)(arow * a.K + achunk * 8) * 2u;
+  // unit i: row 32 i + t / 8 = 16-row tile (t / 128 + 2 i), row (t / 8) % 16
+  const uint32_t q_off = (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + achunk * 2);
+  const uint32_t q_step = (uint32_t)(2 * G * 512);  // two 16-row tiles
+  const uint32_t d_off = (uint32_t)((tid >> 7) * a.d_tile_bytes + ((tid >> 3) & 15) * 16);
+  const uint32_t d_step = (uint32_t)(2 * a.d_tile_bytes);
 
-  // staging registers for two K-tiles: the tile stored during a K-tile's
-  // multiplies was loaded one iteration earlier, so storing it never waits
-  uint4 ra[2][8];
-  uint4 rq[2];
-  float rd[2];
-  auto gload = [&](int kt, int set) {
-    const int64_t k0 = (int64_t)kt * TK;
+  // LDS byte offset of this thread's 16-byte chunk in rows arow + 32 i (A)
+  // and in weight rows arow + 32 i (B): row * 128 + (chunk ^ (row / 2) % 8) * 16,
+  // and (row / 2) % 8 = (t / 16) % 8 for every i
+  const uint32_t w_lds = (uint32_t)(arow * ROWB + ((achunk ^ ((tid >> 4) & 7)) << 4));
+
+  // staging registers: the tile written to LDS at the start of iteration t
+  // was fetched at the start of iteration t - 1
+  uint4 ra[8];
+  uint32_t rq[UNITS];
+  uint32_t rdd[UNITS];
+  auto gload = [&](int kt) {
+    const uint32_t k0 = (uint32_t)kt * TK;
+    const uint32_t rowstep = (uint32_t)(32 * a.K * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      ra[set][i] = buffer_load_16B(ra_rs, a_off + (uint32_t)((32 * i * a.K + k0) * 2));
-    rq[set] = buffer_load_16B(rq_rs, q_off + (uint32_t)((k0 >> 7) * 512 + ((k0 & 127) >> 2)));
-    rd[set] = f16_bits_to_f32(buffer_load_2B(rd_rs, d_off + (uint32_t)((k0 >> 10) * 256 + ((k0 >> 7) & 7) * 2)));
-  };
-  auto sstore = [&](int buf, int set) {
-    uint16_t* A = smem + buf * STAGE_ELEMS;
-    uint16_t* B = A + TM * LDK;
+    for (int i = 0; i < 8; ++i) ra[i] = load16_s(ra_rs, a_off, k0 * 2 + i * rowstep);
+    const uint32_t qk = (k0 >> 7) * 512 + ((k0 & 127) >> 2);
+    const uint32_t dk = (k0 >> 10) * 256 + ((k0 >> 7) & 7) * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(A + (32 * i + arow) * LDK + achunk) = ra[set][i];
-    {
-      uint32_t b8[32];
-      dequant_word_bf16(rq[set].x, rd[set], b8);
-      dequant_word_bf16(rq[set].y, rd[set], b8 + 8);
-      dequant_word_bf16(rq[set].z, rd[set], b8 + 16);
-      dequant_word_bf16(rq[set].w, rd[set], b8 + 24);
-      uint4* pb = reinterpret_cast<uint4*>(B + tid * LDK);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = make_uint4(b8[4 * i], b8[4 * i + 1], b8[4 * i + 2], b8[4 * i + 3]);
+    for (int i = 0; i < UNITS; ++i) {
+      rq[i] = load2_s(rq_rs, q_off, qk + i * q_step);
+      rdd[i] = load2_s(rd_rs, d_off, dk + i * d_step);
     }
+  };
+  auto sstore = [&](int stage) {
+    uint8_t* S = smem + stage * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(S + w_lds + i * 32 * ROWB) = ra[i];
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i)
+      *reinterpret_cast<uint4*>(S + A_BYTES + w_lds + i * 32 * ROWB) =
+          dequant8_bf16(rq[i], f16_bits_to_f32(rdd[i]));
   };
 
   f32x4 acc[FM][FN];
@@ -159,70 +174,92 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int KT = (int)(a.K / TK);  // even: K is a multiple of 128
-  gload(0, 0);
-  gload(1, 1);
-  sstore(0, 0);
-  __syncthreads();
+  // operand rows: lane (r, kq) reads 8 bf16 at k = 32 ks + 8 kq of row r of a
+  // 16-row tile; swizzled chunk (4 ks + kq) ^ (r / 2) % 8 (rows of a tile
+  // start at multiples of 16, so (row / 2) % 8 = (r / 2) % 8)
+  const int fr = lane & 15, kq = lane >> 4;
+  const uint32_t sw = (uint32_t)((kq ^ (fr >> 1)) & 7) << 4;
+  // k-step 1 flips chunk bit 2 (byte 64); row and tile offsets leave it clear
+  const uint32_t a_rd0 = (uint32_t)((wm * WM + fr) * ROWB) + sw;
+  const uint32_t b_rd0 = (uint32_t)(A_BYTES + (wn * WN + fr) * ROWB) + sw;
+  const uint32_t a_rd1 = a_rd0 ^ 64u, b_rd1 = b_rd0 ^ 64u;
+  // one set of A operands, refilled row tile by row tile as the MFMAs release
+  // them; two sets of B operands (all five are used by every row tile)
+  bf16x8 fa[FM], fb[2][FN];
+  auto lda = [&](int stage, int ks, int i) {
+    return *reinterpret_cast<const bf16x8*>(smem + stage * STAGE_BYTES + (ks ? a_rd1 : a_rd0) + i * 16 * ROWB);
+  };
+  auto ldb = [&](int stage, int ks, int j) {
+    return *reinterpret_cast<const bf16x8*>(smem + stage * STAGE_BYTES + (ks ? b_rd1 : b_rd0) + j * 16 * ROWB);
+  };
+  // the 40 MFMAs of one k-step with B set `cur`, reading the operands of the
+  // next k-step (stage `ns`, k-step `nks`) into A and B set `cur ^ 1`
+  auto mma = [&](int cur, int ns, int nks) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cur][j], acc[i][j], 0, 0, 0);
+      fa[i] = lda(ns, nks, i);
+      if (i < FN) fb[cur ^ 1][i] = ldb(ns, nks, i);
+    }
+  };
 
-  // operand rows: lane (r, kq) reads 8 bf16 at k = 8 kq of row r of a 16-row tile
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  auto mma_tile = [&](int buf) {
-    const uint16_t* A = smem + buf * STAGE_ELEMS + (wm * WM + fr) * LDK + fk;
-    const uint16_t* B = smem + buf * STAGE_ELEMS + TM * LDK + (wn * WN + fr) * LDK + fk;
-#pragma unroll
-    for (int ks = 0; ks < TK / 32; ++ks) {
-      bf16x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(A + i * 16 * LDK + ks * 32);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(B + j * 16 * LDK + ks * 32);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-  };
-  // K-tile kt: multiply buffer kt % 2, store tile kt + 1 (staged in set
-  // (kt + 1) % 2) into the other buffer, load tile kt + 2 into set kt % 2.
-  // Unrolled by two so buffer and set indices are compile-time constants.
-  // steady state: load, multiply and store in one basic block, with the
-  // staging work (code and x' loads, dequantization, LDS writes) interleaved
-  // between the MFMAs: each MFMA is followed by two vector-ALU slots, the
-  // second k-step's fragment reads ride on the first 13, the LDS writes on
-  // the second 16
-  auto step = [&](int kt, auto BUF) {
-    constexpr int buf = decltype(BUF)::value;
-    gload(kt + 2, buf);
-    mma_tile(buf);
-    sstore(buf ^ 1, buf ^ 1);
-    __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);  // global loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 13, 0);  // fragment reads, k-step 0
-#pragma unroll
-    for (int i = 0; i < 40; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 40; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      if (i < 16) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 3 < KT; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
-  }
-  // last two K-tiles (KT is even): store the final tile, then multiply it
-  mma_tile(0);
-  sstore(1, 1);
+  const int KT = (int)(a.K / TK);  // even: K is a multiple of 128
+  // prologue: tiles 0 and 1 to stages 0 and 1, tiles 2 and 3 in flight,
+  // the first k-step's operands in registers
+  gload(0);
+  sstore(0);
+  gload(1);
   __syncthreads();
-  mma_tile(1);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa[i] = lda(0, 0, i);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fb[0][j] = ldb(0, 0, j);
+
+  // iteration t: stage t % 2 holds tile t.  First half: k-step 0 of tile t
+  // from registers while its k-step 1 is read, tile t + 1 (fetched during
+  // the last iteration) is written to the other stage and tile t + 2 is
+  // fetched.  Second half, after the barrier: k-step 1 while the next tile's
+  // k-step 0 is read.  The other stage was last read before the previous
+  // barrier, so one barrier per tile suffices.
+  auto iter = [&](int t, auto STAGE) {
+    constexpr int st = decltype(STAGE)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    sstore(st ^ 1);
+    gload(t + 2);
+    mma(0, st, 1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j == 1 || j == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    mma(1, st ^ 1, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the last two tiles are peeled off the loop: with them inside, the
+  // compiler moved the accumulators between register files every iteration
+  int t = 0;
+  for (; t + 2 < KT; t += 2) {
+    iter(t, std::integral_constant<int, 0>{});
+    iter(t + 1, std::integral_constant<int, 1>{});
+  }
+  iter(t, std::integral_constant<int, 0>{});
+  iter(t + 1, std::integral_constant<int, 1>{});
 
   // ---- epilogue: lane (j, q), register r -> row 4q + r, column j of a tile
 #pragma unroll

@@ -713,7 +713,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 // in flight: two for one activation row, one for two to four (their digit
 // operands take the registers), two again for the bf16 kernel of five to
 // eight rows, whose waves may use 256 VGPRs (at most 8 waves).
-__host__ __device__ constexpr int q8_rbr(int M) { return M == 1 ? 4 : 2; }  // row blocks per reduction round
+__host__ __device__ constexpr int q8_rbr(int M) { return M == 1 ? 8 : 2; }  // row blocks per reduction round
 __host__ __device__ constexpr int q8_maxw(int M) { return M <= 4 ? 12 : 8; }
 template <int M>
 struct Q8Cfg {
