@@ -82,6 +82,9 @@ __device__ __forceinline__ uint4 load16_s(BufRsrc r, uint32_t voff, uint32_t sof
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint32_t load4_s(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ uint32_t load2_s(BufRsrc r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
@@ -114,10 +117,15 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   }
   const int64_t m0 = (int64_t)m_tile * TM, n0 = (int64_t)n_tile * TN;
 
-  // ---- global load geometry.  x' tile: load i of thread t covers row
-  // 32 i + t / 8, bytes 16 (t % 8) .. +15 of its 128-byte K-tile slice.
-  // Weights: unit i of thread t is weight row 32 i + t / 8, codes
-  // 8 (t % 8) .. +7 of the K-tile (16 bits), with its block's scale.
+  // ---- global load geometry.  K order inside a tile: the two K-tiles of a
+  // 128-element block interleave in runs of 8, so chunk c (8 elements) of
+  // K-tile 2b + h holds elements 16 c + 8 h .. +7 of block b.  The product
+  // is a sum over K, so any order shared by both operands gives it; this one
+  // puts a thread's codes for both K-tiles of a block in one 4-byte word.
+  // x' tile: load i of thread t covers row 32 i + t / 8, chunk t % 8.
+  // Weights: unit i of thread t is weight row 32 i + t / 8, chunk t % 8: 16
+  // bits of a 4-byte word loaded once per block (the low half for the even
+  // K-tile), with the block's scale.
   // All go through buffer resources that cover exactly the block's valid
   // rows, so rows past M or N read zeros with no branch: code 0 with scale 0
   // dequantizes to 0.
@@ -128,9 +136,9 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   const BufRsrc ra_rs = make_rsrc(a.xb + m0 * a.K, (uint32_t)(arows * a.K * 2));
   const BufRsrc rq_rs = make_rsrc(a.qs + (n0 >> 4) * G * 512, (uint32_t)((brows + 15) / 16 * G * 512));
   const BufRsrc rd_rs = make_rsrc(a.dpl + (n0 >> 4) * a.d_tile_bytes, (uint32_t)((brows + 15) / 16 * a.d_tile_bytes));
-  const uint32_t a_off = (uint32_t)(arow * a.K + achunk * 8) * 2u;
+  const uint32_t a_off = (uint32_t)(arow * a.K + achunk * 16) * 2u;
   // unit i: row 32 i + t / 8 = 16-row tile (t / 128 + 2 i), row (t / 8) % 16
-  const uint32_t q_off = (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + achunk * 2);
+  const uint32_t q_off = (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + achunk * 4);
   const uint32_t q_step = (uint32_t)(2 * G * 512);  // two 16-row tiles
   const uint32_t d_off = (uint32_t)((tid >> 7) * a.d_tile_bytes + ((tid >> 3) & 15) * 16);
   const uint32_t d_step = (uint32_t)(2 * a.d_tile_bytes);
@@ -141,31 +149,34 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   const uint32_t w_lds = (uint32_t)(arow * ROWB + ((achunk ^ ((tid >> 4) & 7)) << 4));
 
   // staging registers: the tile written to LDS at the start of iteration t
-  // was fetched at the start of iteration t - 1
+  // was fetched at the start of iteration t - 1; the weight words and scales
+  // of a block are fetched with its even K-tile and serve both
   uint4 ra[8];
   uint32_t rq[UNITS];
   uint32_t rdd[UNITS];
-  auto gload = [&](int kt) {
-    const uint32_t k0 = (uint32_t)kt * TK;
+  auto gload = [&](int kt, bool with_b) {
+    const uint32_t kb = (uint32_t)kt >> 1, h = (uint32_t)kt & 1u;
     const uint32_t rowstep = (uint32_t)(32 * a.K * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = load16_s(ra_rs, a_off, k0 * 2 + i * rowstep);
-    const uint32_t qk = (k0 >> 7) * 512 + ((k0 & 127) >> 2);
-    const uint32_t dk = (k0 >> 10) * 256 + ((k0 >> 7) & 7) * 2;
+    for (int i = 0; i < 8; ++i) ra[i] = load16_s(ra_rs, a_off, (kb * 128 + h * 8) * 2 + i * rowstep);
+    if (with_b) {
+      const uint32_t qk = kb * 512;
+      const uint32_t dk = (kb >> 3) * 256 + (kb & 7) * 2;
 #pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      rq[i] = load2_s(rq_rs, q_off, qk + i * q_step);
-      rdd[i] = load2_s(rd_rs, d_off, dk + i * d_step);
+      for (int i = 0; i < UNITS; ++i) {
+        rq[i] = load4_s(rq_rs, q_off, qk + i * q_step);
+        rdd[i] = load2_s(rd_rs, d_off, dk + i * d_step);
+      }
     }
   };
-  auto sstore = [&](int stage) {
+  auto sstore = [&](int stage, int h) {
     uint8_t* S = smem + stage * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(S + w_lds + i * 32 * ROWB) = ra[i];
 #pragma unroll
     for (int i = 0; i < UNITS; ++i)
       *reinterpret_cast<uint4*>(S + A_BYTES + w_lds + i * 32 * ROWB) =
-          dequant8_bf16(rq[i], f16_bits_to_f32(rdd[i]));
+          dequant8_bf16(rq[i] >> (16 * h), f16_bits_to_f32(rdd[i]));
   };
 
   f32x4 acc[FM][FN];
@@ -208,9 +219,9 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   const int KT = (int)(a.K / TK);  // even: K is a multiple of 128
   // prologue: tiles 0 and 1 to stages 0 and 1, tiles 2 and 3 in flight,
   // the first k-step's operands in registers
-  gload(0);
-  sstore(0);
-  gload(1);
+  gload(0, true);
+  sstore(0, 0);
+  gload(1, false);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa[i] = lda(0, 0, i);
@@ -226,8 +237,8 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   auto iter = [&](int t, auto STAGE) {
     constexpr int st = decltype(STAGE)::value;
     __builtin_amdgcn_sched_barrier(0);
-    sstore(st ^ 1);
-    gload(t + 2);
+    sstore(st ^ 1, st ^ 1);
+    gload(t + 2, st == 0);
     mma(0, st, 1);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
