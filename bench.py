@@ -118,6 +118,32 @@ def extras(kq, inputs, stream, quick):
             "us_per_call": round(t * 1e6, 3), "weight_GBs": round(gbs(wbytes, t), 1),
             "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4)}
     del copies, p8
+    # PQ2_0 gate|up: two 17408 x 5120 sets sharing one activation, one launch
+    # (kq_gemv_multi) against two one-set launches
+    N = 17408
+    sets = []
+    for i in range(2):
+        W = torch.from_numpy(inputs.weights(1006 + i, N, K)).cuda()
+        sets.append(kq.pack(kq.KQ_FMT_PQ2_0, W))
+        del W
+    pairs = [sets] + [[t.clone() for t in sets] for _ in range(5)]
+    x = torch.from_numpy(inputs.activations(2006, 1, K)).cuda()
+    ys = [torch.empty((1, N), device="cuda") for _ in range(2)]
+    wbytes = 2 * N * K // 128 * 34
+    fns = [(lambda c=c: kq.kq_gemv_multi(kq.KQ_FMT_PQ2_0, 2, c, [N, N], K, x, 1, 128, None, ys))
+           for c in pairs]
+    t, _ = time_graph(fns, 20, 3, stream)
+    t /= len(fns)
+    fns = [(lambda c=c: [kq.kq_gemv(kq.KQ_FMT_PQ2_0, c[i], N, K, x, 1, 128, None, 1, ys[i], None, 0)
+                         for i in range(2)]) for c in pairs]
+    t2, _ = time_graph(fns, 20, 3, stream)
+    t2 /= len(fns)
+    out["pq2_gemv_multi_k5120_2x17408"] = {
+        "us_per_call": round(t * 1e6, 3), "weight_GBs": round(gbs(wbytes, t), 1),
+        "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4),
+        "us_two_single_calls": round(t2 * 1e6, 3)}
+    del pairs, sets
+    torch.cuda.empty_cache()
     # PQ2_0 lm_head GEMV K=5120 N=248320 (split-K 1, 2, 4)
     N = 248320
     W = torch.from_numpy(inputs.weights(1003, N, K)).cuda()

@@ -35,7 +35,8 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_EALIGN",
 # exported symbols, in include/kq.h order
 EXPORTS = ("kq_status_string", "kq_packed_bytes", "kq_pack_pq2", "kq_pack_q8",
            "kq_unpack", "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv",
-           "kq_gemm")
+           "kq_gemv_multi", "kq_gemm")
+MAX_SETS = 4
 
 _p = C.c_void_p
 _i64 = C.c_int64
@@ -56,6 +57,9 @@ _lib.kq_workspace_bytes.argtypes = [_i32, C.c_int, _i64, _i64, _i64, _i32, _i32]
 _lib.kq_gemv.restype = C.c_int
 _lib.kq_gemv.argtypes = [C.c_int, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p,
                          C.c_size_t, _p]
+_lib.kq_gemv_multi.restype = C.c_int
+_lib.kq_gemv_multi.argtypes = [C.c_int, _i32, C.POINTER(_p), C.POINTER(_i64), _i64, _p, _i64,
+                               _i32, _p, C.POINTER(_p), _p]
 _lib.kq_gemm.restype = C.c_int
 _lib.kq_gemm.argtypes = [C.c_int, _p, _i64, _i64, _p, C.c_int, _i64, _i32, _p, _p, _p,
                          C.c_size_t, _p]
@@ -139,6 +143,16 @@ def kq_gemv(fmt: int, packed, N: int, K: int, x, M: int, block_len: int, signs,
            "kq_gemv")
 
 
+def kq_gemv_multi(fmt: int, nsets: int, packed, N, K: int, x, M: int, block_len: int, signs,
+                  y, stream=None):
+    """packed, N, y: sequences of nsets entries (host arrays of the C call)."""
+    P = (_p * max(nsets, 1))(*[_ptr(t) for t in packed[:nsets]])
+    Ns = (_i64 * max(nsets, 1))(*[int(n) for n in N[:nsets]])
+    Y = (_p * max(nsets, 1))(*[_ptr(t) for t in y[:nsets]])
+    _check(_lib.kq_gemv_multi(fmt, nsets, P, Ns, K, _ptr(x), M, block_len, _ptr(signs), Y,
+                              _stream(stream)), "kq_gemv_multi")
+
+
 def kq_gemm(fmt: int, packed, N: int, K: int, x, x_dt: int, M: int, block_len: int,
             signs, y, workspace, ws_bytes: int, stream=None):
     _check(_lib.kq_gemm(fmt, _ptr(packed), N, K, _ptr(x), x_dt, M, block_len, _ptr(signs),
@@ -187,6 +201,17 @@ def gemv(fmt: int, packed, N: int, K: int, x, block_len: int, signs=None, split_
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     kq_gemv(fmt, packed, N, K, x, M, block_len, signs, split_k, y, ws, ws.numel(), stream)
+    return y
+
+
+def gemv_multi(fmt: int, packed, N, K: int, x, block_len: int, signs=None, y=None,
+               stream=None):
+    """One launch over several weight sets sharing x; returns the list of y."""
+    import torch
+    M = x.shape[0]
+    if y is None:
+        y = [torch.empty((M, n), dtype=torch.float32, device=x.device) for n in N]
+    kq_gemv_multi(fmt, len(N), packed, N, K, x, M, block_len, signs, y, stream)
     return y
 
 

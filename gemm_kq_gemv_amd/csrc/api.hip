@@ -115,6 +115,29 @@ kq_status kq_gemv(kq_format fmt, const void* packed, int64_t N, int64_t K, const
   return rc == -2 ? KQ_EUNSUPPORTED : launched(rc);
 }
 
+kq_status kq_gemv_multi(kq_format fmt, int32_t nsets, const void* const* packed, const int64_t* N,
+                        int64_t K, const float* x, int64_t M, int32_t block_len,
+                        const int8_t* signs, float* const* y, void* stream) {
+  if (!fmt_ok(fmt) || !packed || !N || !x || !y) return KQ_EINVAL;
+  if (nsets < 1 || nsets > kq::kMaxSets) return KQ_ESHAPE;
+  if (K < 0 || M < 0) return KQ_EINVAL;
+  for (int s = 0; s < nsets; ++s) {
+    if (!packed[s] || !y[s]) return KQ_EINVAL;
+    if (N[s] < 0) return KQ_EINVAL;
+  }
+  for (int s = 0; s < nsets; ++s)
+    if (!shape_ok(fmt, N[s], K)) return KQ_ESHAPE;
+  if (M < 1 || M > 8 || !block_len_ok(block_len) || (block_len > 0 && K % block_len))
+    return KQ_ESHAPE;
+  if (!aligned16(x) || (signs && !aligned16(signs))) return KQ_EALIGN;
+  for (int s = 0; s < nsets; ++s)
+    if (!aligned16(packed[s]) || !aligned16(y[s])) return KQ_EALIGN;
+  if (kq::check_gemv_multi(fmt, nsets, N, K, M, block_len)) return KQ_EUNSUPPORTED;
+  const int rc = kq::launch_gemv_multi(fmt, nsets, packed, N, K, x, M, block_len, signs, y,
+                                       as_stream(stream));
+  return rc == -2 ? KQ_EUNSUPPORTED : launched(rc);
+}
+
 kq_status kq_gemm(kq_format fmt, const void* packed, int64_t N, int64_t K, const void* x,
                   kq_dtype x_dt, int64_t M, int32_t block_len, const int8_t* signs, float* y,
                   void* workspace, size_t ws_bytes, void* stream) {

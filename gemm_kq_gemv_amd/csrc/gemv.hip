@@ -68,6 +68,18 @@ constexpr int64_t kMaxWgBytes = int64_t(1) << 29;
 constexpr int kLdsBudget = 160 * 1024;
 constexpr int kTargetWGs = 256;  // one workgroup per CU
 
+// One weight set of a multi-set call: its planes, output and row blocks, and
+// the first workgroup of the grid that works on it.
+struct GemvSet {
+  const uint8_t* qs;
+  const uint8_t* dpl;
+  float* out;
+  int64_t N;
+  int rb_base, rb_rem;
+  int wg0;
+  int pad;
+};
+
 struct GemvArgs {
   const uint8_t* qs;
   const uint8_t* dpl;
@@ -86,7 +98,52 @@ struct GemvArgs {
   int u_base, u_rem;     // slice s owns rotation blocks [s*u_base + min(s, u_rem), next)
   int log2n;             // rotation block length (0: no transform)
   float inv_sqrt_n;
+  int nsets;             // 1, or up to kMaxSets weight sets sharing x (then S == 1)
+  GemvSet set[kMaxSets];
 };
+
+// The rows of this workgroup: its weight set (a uniform choice), that set's
+// planes and output, and its range of 16-row blocks.  Every set sees the same
+// activation slices and launch shape, so its outputs are bit-identical to a
+// call for that set alone.  (The arguments are never written: a modified
+// copy of them went through scratch memory.)
+struct WgRows {
+  const uint8_t* qs;
+  const uint8_t* dpl;
+  float* out;
+  int64_t N;
+  int rb0, rb1;
+};
+__host__ __device__ __forceinline__ int part_start(int i, int base, int rem);
+// MULTI: a kernel instance for several sets (one-set calls read no set
+// fields, so their prologue starts as early as before).
+template <bool MULTI>
+__device__ __forceinline__ WgRows wg_rows(const GemvArgs& a) {
+  const int b = (int)blockIdx.x;
+  WgRows w;
+  if constexpr (!MULTI) {
+    w.qs = a.qs;
+    w.dpl = a.dpl;
+    w.out = a.out;
+    w.N = a.N;
+    w.rb0 = part_start(b, a.rb_base, a.rb_rem);
+    w.rb1 = part_start(b + 1, a.rb_base, a.rb_rem);
+    return w;
+  }
+  const int s = (1 < a.nsets && b >= a.set[1].wg0) + (2 < a.nsets && b >= a.set[2].wg0) +
+                (3 < a.nsets && b >= a.set[3].wg0);
+  static_assert(kMaxSets == 4, "the selection below lists the sets");
+#define KQ_PICK(f) (s == 0 ? a.set[0].f : s == 1 ? a.set[1].f : s == 2 ? a.set[2].f : a.set[3].f)
+  w.qs = KQ_PICK(qs);
+  w.dpl = KQ_PICK(dpl);
+  w.out = KQ_PICK(out);
+  w.N = KQ_PICK(N);
+  const int base = KQ_PICK(rb_base), rem = KQ_PICK(rb_rem), bx = b - KQ_PICK(wg0);
+#undef KQ_PICK
+  w.rb0 = part_start(bx, base, rem);
+  w.rb1 = part_start(bx + 1, base, rem);
+  return w;
+}
 
 // ---------------------------------------------------------------------------
 // shared device helpers
@@ -225,7 +282,7 @@ __device__ __forceinline__ void slice_groups(const GemvArgs& a, int s, int& g0, 
 
 // fixed-order sum of the wave partials of one round into y (or split partials);
 // each wave leaves KS partials per output, [NW][RBR][M][KS][16]
-__device__ __forceinline__ void reduce_round(const GemvArgs& a, const float* part, int NW, int RBR,
+__device__ __forceinline__ void reduce_round(const WgRows& a, const float* part, int NW, int RBR,
                                              int M, int KS, int rb0, int nrb, int round, int s) {
   const float* pr = part + (round & 1) * NW * RBR * M * KS * kRB;
   for (int it = threadIdx.x; it < RBR * M * kRB; it += blockDim.x) {
@@ -335,7 +392,7 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <int M, bool DALIGN, int EPL>
+template <int M, bool DALIGN, int EPL, bool MULTI>
 __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvArgs a) {
   using C = Pq2Cfg<EPL>;
   constexpr int GS = C::GS, D = C::D, RBR = C::RBR, LPG = C::LPG;
@@ -362,8 +419,8 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   uint8_t* areg = lds + wave * (GS * M * 512);  // its operand bytes
   float* part = reinterpret_cast<float*>(lds + pq2_lds_part_offset(M, NW, GS));
 
-  const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
-  const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
+  const WgRows wr = wg_rows<MULTI>(a);
+  const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
   // ---- activations first (the vector memory counter completes in order).
@@ -415,9 +472,9 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   };
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
-  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
+  const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   // scales: the workgroup's whole 16-row tiles of the scale plane (padding is zero)
-  const BufRsrc rd = make_rsrc(a.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
@@ -676,7 +733,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     for (int i = 0; i < D; ++i)
       if (i < nrb) compute(wb[i], i);
     __syncthreads();
-    reduce_round(a, part, NW, RBR, M, KS, rb0, nrb, 0, blockIdx.y);
+    reduce_round(wr, part, NW, RBR, M, KS, rb0, nrb, 0, blockIdx.y);
     return;
   }
   for (int j0 = 0; j0 < nrb; j0 += D) {
@@ -687,7 +744,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
       issue(j + D, wb[i]);
       if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
         __syncthreads();
-        reduce_round(a, part, NW, RBR, M, KS, rb0, nrb, j / RBR, blockIdx.y);
+        reduce_round(wr, part, NW, RBR, M, KS, rb0, nrb, j / RBR, blockIdx.y);
       }
     }
   }
@@ -803,7 +860,7 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);               // [lo.0, lo.1, hi.0, hi.1]
 }
 
-template <int M, bool DALIGN>
+template <int M, bool DALIGN, bool MULTI>
 __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
   static_assert(M <= 4, "one operand tile: four digits of up to four activation rows");
   constexpr int GS = Q8Cfg<M>::GS, D = Q8Cfg<M>::D, RBR = Q8Cfg<M>::RBR;
@@ -829,8 +886,8 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   float* part = reinterpret_cast<float*>(lds + q8_lds_part_offset(M, NW, GS));
   uint8_t* zeros = lds + q8_lds_zero_offset(M, NW, GS);
 
-  const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
-  const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
+  const WgRows wr = wg_rows<MULTI>(a);
+  const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
   // ---- activation loads first (rows past the first four after the weight
@@ -873,8 +930,8 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   };
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
-  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
-  const BufRsrc rd = make_rsrc(a.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
+  const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
@@ -1092,7 +1149,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
       issue(j + D, wb[i]);
       if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
         __syncthreads();
-        reduce_round(a, part, NW, RBR, M, 4, rb0, nrb, j / RBR, blockIdx.y);
+        reduce_round(wr, part, NW, RBR, M, 4, rb0, nrb, j / RBR, blockIdx.y);
       }
     }
   }
@@ -1113,7 +1170,7 @@ __host__ __device__ inline int q8b_lds_bytes(int M, int NW, int GS) {
   return q8b_lds_part_offset(M, NW, GS) + 2 * NW * q8_rbr(M) * M * kRB * 4;
 }
 
-template <int M, bool DALIGN>
+template <int M, bool DALIGN, bool MULTI>
 __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvArgs a) {
   constexpr int GS = Q8Cfg<M>::GS, D = Q8Cfg<M>::D, RBR = Q8Cfg<M>::RBR;
   constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
@@ -1135,8 +1192,8 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
   float* xs = reinterpret_cast<float*>(lds);  // [M][KRmax]
   float* part = reinterpret_cast<float*>(lds + q8b_lds_part_offset(M, NW, GS));
 
-  const int rb0 = part_start(blockIdx.x, a.rb_base, a.rb_rem);
-  const int rb1 = part_start(blockIdx.x + 1, a.rb_base, a.rb_rem);
+  const WgRows wr = wg_rows<MULTI>(a);
+  const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
   // ---- activation loads first (rows past the first four after the weight
@@ -1179,8 +1236,8 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
   };
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
-  const BufRsrc rq = make_rsrc(a.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
-  const BufRsrc rd = make_rsrc(a.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
+  const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
   auto issue = [&](int j, WBuf& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
@@ -1320,7 +1377,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
       issue(j + D, wb[i]);
       if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
         __syncthreads();
-        reduce_round(a, part, NW, RBR, M, 1, rb0, nrb, j / RBR, blockIdx.y);
+        reduce_round(wr, part, NW, RBR, M, 1, rb0, nrb, j / RBR, blockIdx.y);
       }
     }
   }
@@ -1435,20 +1492,137 @@ static int launch_kernel(Kernel k, const GemvArgs& a, const GemvPlan& p, hipStre
 
 template <int M>
 static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  // several sets: one K slice, so every wave starts on a whole scale run
+  const bool multi = a.nsets > 1;
+  if (multi && !p.dalign) return -1;
   if (fmt == kFmtPQ2) {
     if (p.epl == 8)
-      return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 8>, a, p, st)
-                      : launch_kernel(gemv_pq2_kernel<M, false, 8>, a, p, st);
-    return p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 16>, a, p, st)
-                    : launch_kernel(gemv_pq2_kernel<M, false, 16>, a, p, st);
+      return multi ? launch_kernel(gemv_pq2_kernel<M, true, 8, true>, a, p, st)
+             : p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 8, false>, a, p, st)
+                        : launch_kernel(gemv_pq2_kernel<M, false, 8, false>, a, p, st);
+    return multi ? launch_kernel(gemv_pq2_kernel<M, true, 16, true>, a, p, st)
+           : p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 16, false>, a, p, st)
+                      : launch_kernel(gemv_pq2_kernel<M, false, 16, false>, a, p, st);
   }
   if (p.gs != Q8Cfg<M>::GS) return -1;
   if constexpr (M <= 4)
-    return p.dalign ? launch_kernel(gemv_q8_kernel<M, true>, a, p, st)
-                    : launch_kernel(gemv_q8_kernel<M, false>, a, p, st);
+    return multi ? launch_kernel(gemv_q8_kernel<M, true, true>, a, p, st)
+           : p.dalign ? launch_kernel(gemv_q8_kernel<M, true, false>, a, p, st)
+                      : launch_kernel(gemv_q8_kernel<M, false, false>, a, p, st);
   else
-    return p.dalign ? launch_kernel(gemv_q8_bf16_kernel<M, true>, a, p, st)
-                    : launch_kernel(gemv_q8_bf16_kernel<M, false>, a, p, st);
+    return multi ? launch_kernel(gemv_q8_bf16_kernel<M, true, true>, a, p, st)
+           : p.dalign ? launch_kernel(gemv_q8_bf16_kernel<M, true, false>, a, p, st)
+                      : launch_kernel(gemv_q8_bf16_kernel<M, false, false>, a, p, st);
+}
+
+static int launch_args(int fmt, const GemvArgs& a, const GemvPlan& p, int64_t M, hipStream_t st) {
+  switch (M) {
+    case 1: return launch_m<1>(fmt, a, p, st);
+    case 2: return launch_m<2>(fmt, a, p, st);
+    case 3: return launch_m<3>(fmt, a, p, st);
+    case 4: return launch_m<4>(fmt, a, p, st);
+    case 5: return launch_m<5>(fmt, a, p, st);
+    case 6: return launch_m<6>(fmt, a, p, st);
+    case 7: return launch_m<7>(fmt, a, p, st);
+    default: return launch_m<8>(fmt, a, p, st);
+  }
+}
+
+// fields shared by every weight set: activation, rotation, K geometry
+static void common_args(GemvArgs& a, int fmt, const GemvPlan& p, int64_t K, const float* x,
+                        int block_len, const int8_t* signs) {
+  const PlanarView pv = planar_view(fmt, 1, K, nullptr);
+  a.x = x;
+  a.signs = signs;
+  a.K = K;
+  a.row_bytes = (uint32_t)pv.row_bytes;
+  a.d_tile_bytes = (uint32_t)pv.d_tile_bytes;
+  a.G = (int)(K / (fmt == kFmtPQ2 ? 128 : 32));
+  a.U = p.units;
+  a.S = p.split;
+  a.u_base = (a.G / p.units) / p.split;
+  a.u_rem = (a.G / p.units) % p.split;
+  int log2n = 0;
+  while (block_len > 1 && (1 << log2n) < block_len) ++log2n;
+  a.log2n = log2n;
+  a.inv_sqrt_n = block_len > 1 ? (float)(1.0 / __builtin_sqrt((double)block_len)) : 1.0f;
+  a.nsets = 1;
+}
+
+// Workgroups per weight set: the grid of one launch (kTargetWGs) shared in
+// proportion to each set's row blocks, at least one and at most one per row
+// block each.  Returns the total, or -2 if a set's workgroup slice exceeds
+// the buffer-range limit or no single-slice plan fits.
+static int multi_split(int fmt, int nsets, const int64_t* N, int64_t K, int64_t M, int block_len,
+                       GemvPlan& p, int* wgs) {
+  int64_t nmax = 1, total = 0;
+  for (int s = 0; s < nsets; ++s) {
+    nmax = N[s] > nmax ? N[s] : nmax;
+    total += (N[s] + kRB - 1) / kRB;
+  }
+  p = plan_gemv(fmt, M, nmax, K, block_len, 1);
+  if (p.split != 1) return -2;
+  const int64_t row_bytes = fmt == kFmtPQ2 ? K / 4 : K;
+  int grid = 0;
+  for (int s = 0; s < nsets; ++s) {
+    const int64_t rb = (N[s] + kRB - 1) / kRB;
+    int64_t w = (kTargetWGs * rb + total / 2) / total;
+    w = w < 1 ? 1 : (w > rb ? rb : w);
+    if ((rb + w - 1) / w * kRB * row_bytes > kMaxWgBytes) return -2;
+    wgs[s] = (int)w;
+    grid += (int)w;
+  }
+  return grid;
+}
+
+int check_gemv_multi(int fmt, int nsets, const int64_t* N, int64_t K, int64_t M, int block_len) {
+  GemvPlan p;
+  int wgs[kMaxSets];
+  return multi_split(fmt, nsets, N, K, M, block_len, p, wgs) > 0 ? 0 : -2;
+}
+
+int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64_t* N, int64_t K,
+                      const float* x, int64_t M, int block_len, const int8_t* signs,
+                      float* const* y, hipStream_t st) {
+  GemvPlan p;
+  int wgs[kMaxSets];
+  const int grid = multi_split(fmt, nsets, N, K, M, block_len, p, wgs);
+  if (grid < 1) return -2;
+  GemvArgs a;
+  common_args(a, fmt, p, K, x, block_len, signs);
+  a.nsets = nsets;
+  int wg0 = 0;
+  for (int s = 0; s < kMaxSets; ++s) {
+    GemvSet& w = a.set[s];
+    if (s < nsets) {
+      const PlanarView pv = planar_view(fmt, N[s], K, const_cast<void*>(packed[s]));
+      const int rb = (int)((N[s] + kRB - 1) / kRB);
+      w.qs = pv.qs;
+      w.dpl = pv.d;
+      w.out = y[s];
+      w.N = N[s];
+      w.rb_base = rb / wgs[s];
+      w.rb_rem = rb % wgs[s];
+      w.wg0 = wg0;
+      wg0 += wgs[s];
+    } else {
+      w = a.set[0];
+      w.wg0 = 1 << 30;  // never chosen
+    }
+    w.pad = 0;
+  }
+  // the single-set fields describe set 0; every workgroup replaces them
+  a.qs = a.set[0].qs;
+  a.dpl = a.set[0].dpl;
+  a.out = a.set[0].out;
+  a.N = a.set[0].N;
+  a.rb_base = a.set[0].rb_base;
+  a.rb_rem = a.set[0].rb_rem;
+  a.total_rb = 0;
+  a.grid_x = grid;
+  p.grid_x = grid;
+  if (launch_args(fmt, a, p, M, st) || hipGetLastError() != hipSuccess) return -1;
+  return 0;
 }
 
 int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,
@@ -1458,40 +1632,17 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
   if (p.split < 1) return -2;
   PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
   GemvArgs a;
+  common_args(a, fmt, p, K, x, block_len, signs);
   a.qs = pv.qs;
   a.dpl = pv.d;
-  a.x = x;
-  a.signs = signs;
   a.N = N;
-  a.K = K;
-  a.row_bytes = (uint32_t)pv.row_bytes;
-  a.d_tile_bytes = (uint32_t)pv.d_tile_bytes;
-  a.G = (int)(K / (fmt == kFmtPQ2 ? 128 : 32));
-  a.U = p.units;
-  a.S = p.split;
   a.total_rb = p.total_rb;
   a.grid_x = p.grid_x;
   a.rb_base = p.total_rb / p.grid_x;
   a.rb_rem = p.total_rb % p.grid_x;
-  a.u_base = (a.G / p.units) / p.split;
-  a.u_rem = (a.G / p.units) % p.split;
-  int log2n = 0;
-  while (block_len > 1 && (1 << log2n) < block_len) ++log2n;
-  a.log2n = log2n;
-  a.inv_sqrt_n = block_len > 1 ? (float)(1.0 / __builtin_sqrt((double)block_len)) : 1.0f;
   float* part = p.split > 1 ? (float*)ws : nullptr;
   a.out = p.split > 1 ? part : y;
-  int rc;
-  switch (M) {
-    case 1: rc = launch_m<1>(fmt, a, p, st); break;
-    case 2: rc = launch_m<2>(fmt, a, p, st); break;
-    case 3: rc = launch_m<3>(fmt, a, p, st); break;
-    case 4: rc = launch_m<4>(fmt, a, p, st); break;
-    case 5: rc = launch_m<5>(fmt, a, p, st); break;
-    case 6: rc = launch_m<6>(fmt, a, p, st); break;
-    case 7: rc = launch_m<7>(fmt, a, p, st); break;
-    default: rc = launch_m<8>(fmt, a, p, st); break;
-  }
+  const int rc = launch_args(fmt, a, p, M, st);
   if (rc || hipGetLastError() != hipSuccess) return -1;
   if (p.split > 1) {
     const int64_t n = M * N;

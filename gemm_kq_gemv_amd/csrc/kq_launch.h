@@ -61,6 +61,15 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
                 int block_len, const int8_t* signs, int split_req, float* y, void* ws,
                 hipStream_t st);
 
+// Several weight sets (same K and format) times one activation: one launch,
+// the workgroups split between the sets in proportion to their rows.
+constexpr int kMaxSets = 4;
+// 0 when a launch plan exists, -2 when none fits (as launch_gemv)
+int check_gemv_multi(int fmt, int nsets, const int64_t* N, int64_t K, int64_t M, int block_len);
+int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64_t* N, int64_t K,
+                      const float* x, int64_t M, int block_len, const int8_t* signs,
+                      float* const* y, hipStream_t st);
+
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
                              const void* signs_hint);
 int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_bf16, int64_t M,

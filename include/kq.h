@@ -169,6 +169,27 @@ kq_status kq_gemv(kq_format fmt, const void *packed, int64_t N, int64_t K,
                   const int8_t *signs, int32_t split_k, float *y,
                   void *workspace, size_t ws_bytes, void *stream);
 
+/* Several weight sets times one activation in one launch: for s < nsets,
+ *     y[s][m][n] = sum_k deq(W_s)[n][k] * x'[m][k]
+ * with every W_s an N[s] x K matrix in `fmt` and x' as in kq_gemv (shared:
+ * rotated once per workgroup), so projections fed by the same activation
+ * (q, k and v; gate and up) take a single launch ([BT] sec. 8.7, the matvec
+ * over several weight sets).  packed, N and y are HOST
+ * arrays of nsets entries; packed[s] and y[s] are device pointers (planar
+ * buffer of kq_packed_bytes(fmt, N[s], K) bytes; fp32 [M][N[s]]).  One pass
+ * over K (no split, no workspace).  Each y[s] is bit-identical to
+ * kq_gemv(fmt, packed[s], N[s], K, x, M, block_len, signs, 1, y[s], ...):
+ * same arithmetic, same fixed reduction order.  The outputs may not overlap
+ * each other or x.
+ * Errors: KQ_EINVAL (NULL array or entry, negative size), KQ_ESHAPE (nsets
+ * not in 1..4, or as kq_gemv for any set), KQ_EALIGN, KQ_EUNSUPPORTED (no
+ * one-slice plan: the K slice does not fit one workgroup's LDS, or more than
+ * 512 MiB of codes per workgroup), KQ_EDEVICE. */
+kq_status kq_gemv_multi(kq_format fmt, int32_t nsets, const void *const *packed,
+                        const int64_t *N, int64_t K, const float *x, int64_t M,
+                        int32_t block_len, const int8_t *signs, float *const *y,
+                        void *stream);
+
 /* Prefill GEMM (many tokens) for PQ2_0 weights, dequantize-once-per-tile
  * ([KB] "Quantized projections on the tensor units"; [BT] 8.3 tiled GEMM):
  *     y[m][n] = sum_k bf16(deq(W)[n][k]) * bf16(x'[m][k])   (fp32 accumulate)

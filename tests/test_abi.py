@@ -156,3 +156,25 @@ def test_gemm_rejections():
     assert _status(g, 1, FAKE, 64, 128, FAKE, 1, 4, 128, None, FAKE, None, 0, 0) == "KQ_EWORKSPACE"
     assert _status(g, 1, FAKE, 64, 128, FAKE, 0, 4, 0, None, FAKE, FAKE, 16, 0) == "KQ_EWORKSPACE"
     assert _status(g, 1, FAKE, 64, 128, FAKE, 1, 4, 128, None, MISALIGNED, FAKE, ws, 0) == "KQ_EALIGN"
+
+
+@pytest.mark.usefixtures("nogpu")
+def test_gemv_multi_rejections():
+    kq = _lib()
+    g = kq.kq_gemv_multi
+    two = [FAKE, FAKE]
+    assert _status(g, 3, 2, two, [64, 64], 128, FAKE, 1, 128, None, two, 0) == "KQ_EINVAL"
+    assert _status(g, 1, 2, [FAKE, None], [64, 64], 128, FAKE, 1, 128, None, two, 0) == "KQ_EINVAL"
+    assert _status(g, 1, 2, two, [64, 64], 128, None, 1, 128, None, two, 0) == "KQ_EINVAL"
+    assert _status(g, 1, 2, two, [64, 64], 128, FAKE, 1, 128, None, [FAKE, None], 0) == "KQ_EINVAL"
+    assert _status(g, 1, 2, two, [64, -1], 128, FAKE, 1, 128, None, two, 0) == "KQ_EINVAL"
+    assert _status(g, 1, 0, two, [64, 64], 128, FAKE, 1, 128, None, two, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, 5, [FAKE] * 5, [64] * 5, 128, FAKE, 1, 128, None, [FAKE] * 5, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, 2, two, [64, 0], 128, FAKE, 1, 128, None, two, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, 2, two, [64, 64], 192, FAKE, 1, 128, None, two, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, 2, two, [64, 64], 128, FAKE, 9, 128, None, two, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, 2, two, [64, 64], 384, FAKE, 1, 256, None, two, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, 2, [FAKE, MISALIGNED], [64, 64], 128, FAKE, 1, 128, None, two, 0) == "KQ_EALIGN"
+    assert _status(g, 1, 2, two, [64, 64], 128, FAKE, 1, 128, None, [MISALIGNED, FAKE], 0) == "KQ_EALIGN"
+    # one K slice must fit a workgroup: K = 2^20 PQ2_0 codes do not
+    assert _status(g, 1, 2, two, [64, 64], 1 << 20, FAKE, 1, 128, None, two, 0) == "KQ_EUNSUPPORTED"

@@ -223,3 +223,56 @@ def test_all_plus_one_rows_closed_form():
     want = np.sqrt(n) * x[0, ::n].astype(np.float64).sum()
     bound = np.abs(oracle.rotate(x.astype(np.float64), n)).sum()   # sum_k |W x'| with W = 1
     assert np.all(np.abs(y[0] - want) <= TOL * bound)
+
+
+# ---- several weight sets in one launch ----------------------------------------
+
+def _multi(fmt, Ws, x, block_len, signs=None):
+    """kq_gemv_multi over the sets of Ws (each packed on the GPU), outputs in
+    guarded buffers; returns (outputs, packed buffers)."""
+    kq = _kq()
+    K = Ws[0].shape[1]
+    M = x.shape[0]
+    packed = [kq.pack(fmt, dev(W)) for W in Ws]
+    outs = [guarded_empty((M, W.shape[0])) for W in Ws]
+    kq.kq_gemv_multi(fmt, len(Ws), packed, [W.shape[0] for W in Ws], K, dev(x), M, block_len,
+                     None if signs is None else dev(signs), [y for y, _ in outs])
+    ys = [host(y) for y, _ in outs]
+    for (y, buf), W in zip(outs, Ws):
+        check_guard(buf, M * W.shape[0])
+    return ys, packed
+
+
+@pytest.mark.parametrize("fmt,M", [(1, 1), (1, 3), (1, 8), (2, 1), (2, 4), (2, 6)])
+@pytest.mark.parametrize("Ns", [(300, 77), (1024, 16, 257), (640, 640, 48, 1)])
+def test_multi_sets_match_single_calls(fmt, M, Ns):
+    """Each set's output is the oracle's within the GEMV bound and bitwise the
+    one-set call's (same plan, same fixed reduction order)."""
+    kq = _kq()
+    K = 2048
+    Ws = [inputs.weights(1400 + 7 * i + len(Ns), n, K) for i, n in enumerate(Ns)]
+    x = inputs.activations(1450 + M, M, K, offset=0.1)
+    bl = 128 if fmt == 1 else 32
+    s = inputs.signs(1460, K)
+    ys, packed = _multi(fmt, Ws, x, bl, s)
+    for i, (W, y, p) in enumerate(zip(Ws, ys, packed)):
+        y_ref, b = _oracle_ref(fmt, W, x, bl, s)
+        assert_within_bound(y, y_ref, b, TOL, f"set {i} of {Ns}")
+        one = host(kq.gemv(fmt, p, W.shape[0], K, dev(x), bl, dev(s), split_k=1))
+        assert np.array_equal(y.view(np.uint32), one.view(np.uint32)), f"set {i} differs from its own call"
+
+
+def test_multi_gate_up_full_size_sampled():
+    """Two PQ2_0 sets of 17408 x 5120 (gate and up), one activation row:
+    sampled rows against the oracle, every row bitwise against one-set calls."""
+    kq = _kq()
+    N, K = 17408, 5120
+    Ws = [inputs.weights(1470 + i, N, K) for i in range(2)]
+    x = inputs.activations(1480, 1, K)
+    ys, packed = _multi(1, Ws, x, 128)
+    rows = np.unique(np.concatenate([inputs.rng(11).integers(0, N, 400), [0, N - 1]]))
+    for i, (W, y, p) in enumerate(zip(Ws, ys, packed)):
+        y_ref, b = _oracle_ref(1, W[rows], x, 128)
+        assert_within_bound(y[:, rows], y_ref, b, TOL, f"gate/up set {i}")
+        one = host(kq.gemv(1, p, N, K, dev(x), 128, split_k=1))
+        assert np.array_equal(y.view(np.uint32), one.view(np.uint32))
