@@ -150,6 +150,7 @@ kq_status kq_gemm(kq_format fmt, const void* packed, int64_t N, int64_t K, const
   if (!aligned16(packed) || !aligned16(x) || !aligned16(y) || (signs && !aligned16(signs)) ||
       (workspace && !aligned16(workspace)))
     return KQ_EALIGN;
+  if (!kq::gemm_shape_supported(M, N, K)) return KQ_EUNSUPPORTED;
   const int64_t need = kq::gemm_workspace_bytes(M, N, K, block_len, x_dt == KQ_BF16, signs);
   const bool uses_ws = block_len > 0 || signs || x_dt != KQ_BF16;
   if (uses_ws && (!workspace || (int64_t)ws_bytes < need)) return KQ_EWORKSPACE;

@@ -127,8 +127,10 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   // bits of a 4-byte word loaded once per block (the low half for the even
   // K-tile), with the block's scale.
   // All go through buffer resources that cover exactly the block's valid
-  // rows, so rows past M or N read zeros with no branch: code 0 with scale 0
-  // dequantizes to 0.
+  // rows (the code and scale resources: its valid 16-row tiles, whose rows
+  // past N hold zero codes and zero scales), with the whole offset in the
+  // range-checked vector offset, so rows past M or N read zeros with no
+  // branch: code 0 with scale 0 dequantizes to 0.
   const int arow = tid >> 3, achunk = tid & 7;
   const int64_t G = a.d_per_row;
   const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
@@ -151,21 +153,28 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   // staging registers: the tile written to LDS at the start of iteration t
   // was fetched at the start of iteration t - 1; the weight words and scales
   // of a block are fetched with its even K-tile and serve both
+  const int KT = (int)(a.K / TK);  // even: K is a multiple of 128
   uint4 ra[8];
   uint32_t rq[UNITS];
   uint32_t rdd[UNITS];
+  // Every offset goes into the per-lane (vector) offset: the hardware range
+  // check of a raw buffer load covers the vector offset only, not the scalar
+  // one.  K-tiles past the end (the prefetches of the last two iterations)
+  // load at kOutOfRange.
   auto gload = [&](int kt, bool with_b) {
+    const bool in_k = kt < KT;
     const uint32_t kb = (uint32_t)kt >> 1, h = (uint32_t)kt & 1u;
     const uint32_t rowstep = (uint32_t)(32 * a.K * 2);
+    const uint32_t ak = a_off + (kb * 128 + h * 8) * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = load16_s(ra_rs, a_off, (kb * 128 + h * 8) * 2 + i * rowstep);
+    for (int i = 0; i < 8; ++i) ra[i] = load16_s(ra_rs, in_k ? ak + i * rowstep : kOutOfRange, 0);
     if (with_b) {
-      const uint32_t qk = kb * 512;
-      const uint32_t dk = (kb >> 3) * 256 + (kb & 7) * 2;
+      const uint32_t qk = q_off + kb * 512;
+      const uint32_t dk = d_off + (kb >> 3) * 256 + (kb & 7) * 2;
 #pragma unroll
       for (int i = 0; i < UNITS; ++i) {
-        rq[i] = load4_s(rq_rs, q_off, qk + i * q_step);
-        rdd[i] = load2_s(rd_rs, d_off, dk + i * d_step);
+        rq[i] = load4_s(rq_rs, in_k ? qk + i * q_step : kOutOfRange, 0);
+        rdd[i] = load2_s(rd_rs, in_k ? dk + i * d_step : kOutOfRange, 0);
       }
     }
   };
@@ -216,7 +225,6 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
     }
   };
 
-  const int KT = (int)(a.K / TK);  // even: K is a multiple of 128
   // prologue: tiles 0 and 1 to stages 0 and 1, tiles 2 and 3 in flight,
   // the first k-step's operands in registers
   gload(0, true);
@@ -285,6 +293,15 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+// 32-bit buffer ranges and offsets: a 256-row x' tile spans 512 K bytes,
+// which must stay below the out-of-range offset (kOutOfRange, about 2^31);
+// the tile grid must fit an int.
+bool gemm_shape_supported(int64_t M, int64_t N, int64_t K) {
+  if (K > kGemmMaxK) return false;
+  const int64_t mt = (M + TM - 1) / TM, nt = (N + TN - 1) / TN;
+  return mt * nt <= 0x7FFFFFFF;
 }
 
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,

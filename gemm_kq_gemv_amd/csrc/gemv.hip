@@ -10,16 +10,15 @@
 // The product is bandwidth-bound, so the arithmetic has to stay well under
 // one vector instruction per weight.  The multiply-adds go to the matrix
 // cores and the vector ALUs only unpack:
-// * PQ2_0.  A 2-bit code c masked into the low bits of a nibble IS an E2M1
-//   (fp4) number equal to c/2, so (w & 0x33333333) and ((w >> 2) &
-//   0x33333333) turn one 32-bit word into 16 fp4 operands with three bit
-//   operations.  v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 weight rows
-//   x 128 codes (one quantization group) by a 16-row operand that holds x' as
-//   four e5m2 terms (|x' - (t0 + t1 + t2 + t3)| <= 2^-12 |x'|) for up to four
-//   activation rows.  The ternary map's -1 is folded in with the group sum X
-//   of the same terms: sum (c-1) x' = 2 sum (c/2) x' - X (the Bonsai page,
-//   sec. 8.5, folds the -1 into an activation sum as well).  Each group of x'
-//   is scaled by its own power of two first, so its range suits e5m2.
+// * PQ2_0.  Three or four bit operations per 32-bit word turn 16 2-bit codes
+//   into 16 signed E2M1 (fp4) operands of value (c - 1) / 2, so that
+//   v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 weight rows x 128 codes
+//   (one quantization group) by a 16-row operand that holds x' as four e5m2
+//   terms (|x' - (t0 + t1 + t2 + t3)| <= 2^-12 |x'|) for up to four
+//   activation rows.  Each group of x' is scaled by its own power of two
+//   first, so its range suits e5m2.  A zero weight is a zero operand: the
+//   matrix core aligns the products of one instruction to the largest of
+//   them, so only weights that count may set that scale.
 // * Q8_0, up to four activation rows.  The int8 weights go into
 //   v_mfma_i32_16x16x32_i8 as loaded; x' enters as four int8 digits of 7 bits
 //   under a power-of-two scale per row, the integer sums convert to fp32
@@ -270,6 +269,23 @@ __device__ __forceinline__ void pair_to_operands(const uint4& v, uint2& g0, uint
   g1 = make_uint2(z, w);
 }
 
+// The 16 2-bit codes of one word (code j at bits 2j) as signed E2M1 (fp4)
+// operands of value (c - 1) / 2: code 0 -> -0.5 (1001), 1 -> -0 (1000),
+// 2 -> +0.5 (0001), and the never-written code 3 -> +1 (0010).  Even codes go
+// to the nibbles of `ev`, odd ones to those of `od` (code 2i and 2i+1 to nibble
+// i).  Nibble bits: [3] = ~b1, [1] = b1 & b0, [0] = ~b0.  Signed operands
+// keep every product of a zero weight at zero: the matrix core sums the
+// products of one instruction aligned to the largest of them, so the smaller
+// ones keep only about 2^-17 of it, and that must be measured against the
+// output's own sum of |w x'| (a form with a constant offset added to every
+// weight lets a large activation element with a zero weight set that scale).
+__device__ __forceinline__ void ternary_fp4(uint32_t w, uint32_t& ev, uint32_t& od) {
+  const uint32_t n = ~w;
+  const uint32_t p = w & (w << 1);  // bit 2j + 1: b1 & b0 of code j
+  ev = (n & 0x11111111u) | ((n << 2) & 0x88888888u) | (p & 0x22222222u);
+  od = ((n >> 2) & 0x11111111u) | (n & 0x88888888u) | ((p >> 2) & 0x22222222u);
+}
+
 // start of part i when parts of `base` items get one more for i < rem
 __host__ __device__ __forceinline__ int part_start(int i, int base, int rem) {
   return i * base + (i < rem ? i : rem);
@@ -368,11 +384,11 @@ __device__ __forceinline__ void rotate(float (&v)[NV], int log2n) {
     default: break;  // 0: no transform
   }
 }
-// max (of values >= 0) / sum over the LPG lanes of one 128-group (8 lanes:
+// max (of values >= 0) over the LPG lanes of one 128-group (8 lanes:
 // a half row, 16: a row).  Pairs: xor 1, xor 2 within quads, then the half-row
 // and row mirrors (lane i with 7 - i, 15 - i), which pair each quad with the
-// other quad and each half with the other half; both lanes of a pair add the
-// same two values, so every lane ends with the same bits.  Non-negative
+// other quad and each half with the other half; both lanes of a pair combine
+// the same two values, so every lane ends with the same bits.  Non-negative
 // binary32 values order like their bit patterns, so the max is an integer one.
 template <int LPG>
 __device__ __forceinline__ float group_max(float v) {
@@ -382,14 +398,6 @@ __device__ __forceinline__ float group_max(float v) {
   u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));
   if constexpr (LPG == 16) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));
   return __uint_as_float(u);
-}
-template <int LPG>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  if constexpr (LPG == 16) v += dpp<0x140>(v);
-  return v;
 }
 
 template <int M, bool DALIGN, int EPL, bool MULTI>
@@ -508,15 +516,14 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   issue(0, wb[0]);
 
   // ---- per-wave prologue: rotation, per-group range scale, e5m2 terms
-  float xr[TILES][GS];   // X * 2^-e of (activation row 4*tile + kb, group); every lane if ONE
-  float gsc[TILES][GS];  // 2^-e of that (row, group)
+  float gsc[TILES][GS];  // 2^-e of (activation row 4*tile + kb, group)
   int sa[GS];            // ONE: E8M0 byte of 2^-e per group
 #pragma unroll
   for (int g = 0; g < GS; ++g) sa[g] = 127;
 #pragma unroll
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
-    for (int g = 0; g < GS; ++g) xr[t][g] = gsc[t][g] = 0.f;
+    for (int g = 0; g < GS; ++g) gsc[t][g] = 0.f;
   {
     const int pw = (lane / C::LPW) & 7;              // packed word in the group
     const int half = lane % C::LPW;                  // which half of it (EPL = 8)
@@ -587,31 +594,18 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
           if (live) *reinterpret_cast<uint4*>(dst) = make_uint4(tw[0], tw[1], tw[2], tw[3]);
         }
       }
-      // X = sum of t0 + t1 + t2 + t3 over the group (exact per element)
-      float tsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) tsum += v[i] - r[i];
-      tsum = group_sum<LPG>(tsum);
+      // the lanes whose outputs belong to activation row m take 2^-e of every
+      // group from the group's first lane
       const float inv = ldexpf(1.f, -e);
-      const float xs = tsum * inv;
-      // the lanes whose outputs belong to activation row m take X and 2^-e of
-      // every group from the group's first lane
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        const float xg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xs), LPG * g));
         if constexpr (ONE) {
-          if (g < vg) {
-            xr[0][g] = xg;
-            sa[g] = 127 - __builtin_amdgcn_readlane(e, LPG * g);
-          }
+          if (g < vg) sa[g] = 127 - __builtin_amdgcn_readlane(e, LPG * g);
         } else {
           const float ig = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), LPG * g));
 #pragma unroll
           for (int t = 0; t < TILES; ++t)
-            if (4 * t + kb == m && g < vg) {
-              xr[t][g] = xg;
-              gsc[t][g] = ig;
-            }
+            if (4 * t + kb == m && g < vg) gsc[t][g] = ig;
         }
       }
     }
@@ -658,12 +652,8 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 #pragma unroll
     for (int g = 0; g < GS; ++g) dg[g] = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
     f32x4 Y[TILES];
-    float cr[TILES];
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      Y[t] = zero;
-      cr[t] = 0.f;
-    }
+    for (int t = 0; t < TILES; ++t) Y[t] = zero;
     // Blocks of four groups.  The accumulators are read only after a delay
     // that is tied to them as asm operands: the compiler's wait-state count
     // for this mixed e5m2 x fp4 MFMA was measured to be too short on gfx950,
@@ -674,9 +664,10 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
       f32x4 acc[TILES][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t w0 = wq[4 * h + u].x, w1 = wq[4 * h + u].y;
-        Bq[u] = (i32x8){(int)(w0 & 0x33333333u), (int)((w0 >> 2) & 0x33333333u),
-                        (int)(w1 & 0x33333333u), (int)((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+        uint32_t e0, o0, e1, o1;
+        ternary_fp4(wq[4 * h + u].x, e0, o0);
+        ternary_fp4(wq[4 * h + u].y, e1, o1);
+        Bq[u] = (i32x8){(int)e0, (int)o0, (int)e1, (int)o1, 0, 0, 0, 0};
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -711,18 +702,17 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 #pragma unroll
             for (int i = 0; i < 4; ++i) Y[t][i] = fmaf(ds, acc[t][u][i], Y[t][i]);
           }
-          cr[t] = fmaf(dg[g], xr[t][g], cr[t]);
         }
     }
     float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * KS * kRB;
     if constexpr (ONE) {
-      // lane block kb: term kb; the X correction once, in block 0
-      pw[kb * kRB + r16] = 2.f * Y[0][0] - (kb == 0 ? cr[0] : 0.f);
+      // lane block kb: term kb
+      pw[kb * kRB + r16] = 2.f * Y[0][0];
     } else {
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         const int mo = 4 * t + kb;
-        if (mo < M) pw[mo * kRB + r16] = 2.f * ((Y[t][0] + Y[t][1]) + (Y[t][2] + Y[t][3])) - cr[t];
+        if (mo < M) pw[mo * kRB + r16] = 2.f * ((Y[t][0] + Y[t][1]) + (Y[t][2] + Y[t][3]));
       }
     }
   };
@@ -1494,7 +1484,7 @@ template <int M>
 static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
   // several sets: one K slice, so every wave starts on a whole scale run
   const bool multi = a.nsets > 1;
-  if (multi && !p.dalign) return -1;
+  if (multi && !p.dalign) return -2;  // no launch plan for these arguments
   if (fmt == kFmtPQ2) {
     if (p.epl == 8)
       return multi ? launch_kernel(gemv_pq2_kernel<M, true, 8, true>, a, p, st)
@@ -1504,7 +1494,7 @@ static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t s
            : p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 16, false>, a, p, st)
                       : launch_kernel(gemv_pq2_kernel<M, false, 16, false>, a, p, st);
   }
-  if (p.gs != Q8Cfg<M>::GS) return -1;
+  if (p.gs != Q8Cfg<M>::GS) return -2;
   if constexpr (M <= 4)
     return multi ? launch_kernel(gemv_q8_kernel<M, true, true>, a, p, st)
            : p.dalign ? launch_kernel(gemv_q8_kernel<M, true, false>, a, p, st)
@@ -1621,8 +1611,9 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
   a.total_rb = 0;
   a.grid_x = grid;
   p.grid_x = grid;
-  if (launch_args(fmt, a, p, M, st) || hipGetLastError() != hipSuccess) return -1;
-  return 0;
+  const int rc = launch_args(fmt, a, p, M, st);
+  if (rc) return rc;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* x, int64_t M,
@@ -1643,7 +1634,8 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
   float* part = p.split > 1 ? (float*)ws : nullptr;
   a.out = p.split > 1 ? part : y;
   const int rc = launch_args(fmt, a, p, M, st);
-  if (rc || hipGetLastError() != hipSuccess) return -1;
+  if (rc) return rc;
+  if (hipGetLastError() != hipSuccess) return -1;
   if (p.split > 1) {
     const int64_t n = M * N;
     splitk_reduce_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(part, y, n, p.split);

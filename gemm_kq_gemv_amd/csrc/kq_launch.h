@@ -1,4 +1,4 @@
-// kq_launch.h -- host-side launch entry points between the C ABI (api.cpp)
+// kq_launch.h -- host-side launch entry points between the C ABI (api.hip)
 // and the kernels.  Shapes reaching these functions are already validated.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -37,7 +37,8 @@ inline PlanarView planar_view(int fmt, int64_t N, int64_t K, void* base) {
   return v;
 }
 
-// All return 0 on success, -1 if the HIP runtime rejected a launch.
+// All return 0 on success, -1 if the HIP runtime rejected a launch (launch_gemv
+// and launch_gemv_multi: -2 if no launch plan fits the arguments).
 int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed, hipStream_t st);
 int launch_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W, hipStream_t st);
 int launch_hadamard(const void* x, int x_bf16, void* xr, int xr_bf16, int64_t M, int64_t K,
@@ -70,6 +71,10 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
                       const float* x, int64_t M, int block_len, const int8_t* signs,
                       float* const* y, hipStream_t st);
 
+// Largest K the prefill GEMM takes: a 256-row activation tile (256 * K * 2
+// bytes) stays a 32-bit buffer range well below the out-of-range offset.
+constexpr int64_t kGemmMaxK = int64_t(1) << 21;
+bool gemm_shape_supported(int64_t M, int64_t N, int64_t K);
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
                              const void* signs_hint);
 int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_bf16, int64_t M,

@@ -141,17 +141,27 @@ size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N,
                           int64_t K, int32_t block_len, int32_t split_k);
 
 /* Quantized GEMV for M in 1..8 activation rows (one decode step, or a few
- * sequences sharing the weights):
+ * sequences sharing the weights).  The folded linear of [BT] 4.2 (sign flip,
+ * blockwise transform, then the ternary matvec y = W' (R x)), with the
+ * PQ2_0 decode of [BT] 3.1 or the Q8_0 decode d*q of [KA] "Weight
+ * quantization" / [KB] (one decode kernel per token, reading every weight
+ * once for all M rows):
  *     y[m][n] = sum_k deq(W)[n][k] * x'[m][k],   x' = rotation of x
  * with deq as in kq_unpack and x' as in kq_hadamard_blocks (block_len 0:
  * x' = x (.) s, no transform).  x is fp32 [M][K]; y is fp32 [M][N].
  * Arithmetic: x' in fp32, codes decoded exactly, fp32 accumulation; each
  * output is within 1e-3 * sum_k |deq(W)[n][k] x'[m][k]| of the exact value.
- * Representation limits (outside them that bound can fail for an output whose
- * weights touch only the small elements): PQ2_0 holds each x' element to
- * 2^-12 of itself down to about 2^-30 of the largest |x'| in its 128-group;
- * Q8_0 with M <= 4 holds each element to 2^-27 of the largest |x'| of its
- * row within the K slice (M >= 5: 2^-17 of itself).
+ * Representation limits: PQ2_0 carries each x' element as four e5m2 terms
+ * (to 2^-12 of itself, down to about 2^-30 of the largest |x'| in its
+ * 128-group), and the matrix core adds the 128 products of a group aligned to
+ * the largest of them, keeping about 17 bits below it; a group whose largest
+ * |w x'| dwarfs the rest can therefore lose up to about 2^-10 of that
+ * product (measured: 7.7e-4 of the bound for an element 2^24 times the others
+ * with no rotation; near 1e-6 of it with a 128-element rotation, which spreads
+ * such elements over the block).  Q8_0 with M <= 4 holds each element to
+ * 2^-27 of the largest |x'| of its row within the K slice (an output whose
+ * weights touch only elements more than about 10^5 below that can miss the
+ * bound); M >= 5: 2^-17 of itself.
  * split_k: 1 = one pass over K; S > 1 splits K into S contiguous ranges of
  * whole blocks whose fp32 partial sums are added in ascending order
  * (deterministic, no atomics); 0 = chosen by the library.  Results are
@@ -197,7 +207,9 @@ kq_status kq_gemv_multi(kq_format fmt, int32_t nsets, const void *const *packed,
  * y is fp32 [M][N].  Each output is within 1e-2 * sum_k |deq(W) x'| of the
  * exact value.  M >= 1, N >= 1, K % 128 == 0.  workspace: at least
  * kq_workspace_bytes(1, ...) bytes (the bf16 x').
- * Errors: as kq_gemv; KQ_EUNSUPPORTED for fmt other than KQ_FMT_PQ2_0. */
+ * Errors: as kq_gemv; KQ_EUNSUPPORTED for fmt other than KQ_FMT_PQ2_0, for
+ * K > 2^21 (32-bit buffer ranges of a 256-row activation tile) or for more
+ * than 2^31 - 1 output tiles. */
 kq_status kq_gemm(kq_format fmt, const void *packed, int64_t N, int64_t K,
                   const void *x, kq_dtype x_dt, int64_t M, int32_t block_len,
                   const int8_t *signs, float *y, void *workspace,

@@ -156,6 +156,9 @@ def test_gemm_rejections():
     assert _status(g, 1, FAKE, 64, 128, FAKE, 1, 4, 128, None, FAKE, None, 0, 0) == "KQ_EWORKSPACE"
     assert _status(g, 1, FAKE, 64, 128, FAKE, 0, 4, 0, None, FAKE, FAKE, 16, 0) == "KQ_EWORKSPACE"
     assert _status(g, 1, FAKE, 64, 128, FAKE, 1, 4, 128, None, MISALIGNED, FAKE, ws, 0) == "KQ_EALIGN"
+    # 32-bit buffer ranges: K above 2^21, or more output tiles than an int holds
+    assert _status(g, 1, FAKE, 64, (1 << 21) + 128, FAKE, 1, 4, 0, None, FAKE, FAKE, ws, 0) == "KQ_EUNSUPPORTED"
+    assert _status(g, 1, FAKE, 1 << 32, 128, FAKE, 1, 1 << 32, 0, None, FAKE, FAKE, ws, 0) == "KQ_EUNSUPPORTED"
 
 
 @pytest.mark.usefixtures("nogpu")

@@ -77,7 +77,7 @@ def c3_inputs():
     return W, packed
 
 
-@pytest.mark.parametrize("split_k", [2, 4])
+@pytest.mark.parametrize("split_k", [1, 2, 4, 0])
 def test_c3_pq2_lm_head_full_size_sampled(split_k, c3_inputs):
     """N = 248320 on the GPU, checked on 1500 sampled rows (plus the ends)."""
     N, K = 248320, 5120
@@ -135,6 +135,46 @@ def test_block_lengths(block_len):
     s = inputs.signs(702, K) if block_len in (0, 1024) else None
     y_ref, b = _oracle_ref(1, W, x, block_len, s)
     assert_within_bound(_run(1, W, x, block_len, s), y_ref, b, TOL, f"n={block_len}")
+
+
+@pytest.mark.parametrize("M", [2, 4, 5, 8])
+@pytest.mark.parametrize("block_len", [512, 1024])
+def test_block_lengths_many_rows(M, block_len):
+    """PQ2_0 with several activation rows at the widest rotation blocks: the
+    1024-block instances hold 16 elements per lane and load rows past the
+    first inside the prologue; two operand tiles from five rows on."""
+    N, K = 300, 5120
+    W = inputs.weights(703 + M, N, K)
+    x = inputs.activations(704 + M, M, K, offset=0.3)
+    s = inputs.signs(705, K)
+    y_ref, b = _oracle_ref(1, W, x, block_len, s)
+    assert_within_bound(_run(1, W, x, block_len, s), y_ref, b, TOL, f"n={block_len} M={M}")
+    assert_within_bound(_run(1, W, x, block_len, s, split_k=5), y_ref, b, TOL,
+                        f"n={block_len} M={M} S=5")
+
+
+# Activations shaped like an LLM's: a few outlier channels 10^3 - 10^4 times
+# the typical magnitude, on top of a DC offset.  Inside the representation
+# envelope kq.h states, so the 1e-3 bound must hold.
+def _outlier_activations(seed, M, K):
+    x = inputs.activations(seed, M, K, offset=0.75)
+    r = inputs.rng(seed + 1)
+    ch = r.choice(K, size=6, replace=False)
+    mag = np.array([1e3, -2e3, 4e3, -1e4, 1e4, 3e3], np.float32)
+    x[:, ch] = mag[None, :] * (1.0 + 0.1 * r.standard_normal((M, 6)).astype(np.float32))
+    return x
+
+
+@pytest.mark.parametrize("fmt,M,block_len", [(1, 1, 128), (1, 3, 128), (1, 8, 1024), (1, 1, 0),
+                                             (2, 1, 0), (2, 4, 0), (2, 5, 0), (2, 8, 0),
+                                             (2, 2, 128)])
+def test_outlier_channels(fmt, M, block_len):
+    N, K = 400, 5120
+    W = inputs.weights(1900 + M, N, K)
+    x = _outlier_activations(1910 + M, M, K)
+    y_ref, b = _oracle_ref(fmt, W, x, block_len)
+    assert_within_bound(_run(fmt, W, x, block_len), y_ref, b, TOL,
+                        f"outliers fmt {fmt} M {M} n {block_len}")
 
 
 @pytest.mark.parametrize("M", [1, 3])
@@ -260,6 +300,37 @@ def test_multi_sets_match_single_calls(fmt, M, Ns):
         assert_within_bound(y, y_ref, b, TOL, f"set {i} of {Ns}")
         one = host(kq.gemv(fmt, p, W.shape[0], K, dev(x), bl, dev(s), split_k=1))
         assert np.array_equal(y.view(np.uint32), one.view(np.uint32)), f"set {i} differs from its own call"
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_multi_sets_block_1024(M):
+    """Several PQ2_0 sets at the 1024-element rotation block (16 elements per
+    lane in the prologue, the multi-set kernel instances)."""
+    kq = _kq()
+    # eight rows of 4 e5m2 terms at 5120 take more operand LDS than one
+    # workgroup has (the call is rejected, see below); 3072 fits
+    K = 5120 if M < 8 else 3072
+    Ns = (300, 77, 520)
+    Ws = [inputs.weights(1490 + 3 * i + M, n, K) for i, n in enumerate(Ns)]
+    x = inputs.activations(1495 + M, M, K, offset=-0.2)
+    s = inputs.signs(1496, K)
+    ys, packed = _multi(1, Ws, x, 1024, s)
+    for i, (W, y, p) in enumerate(zip(Ws, ys, packed)):
+        y_ref, b = _oracle_ref(1, W, x, 1024, s)
+        assert_within_bound(y, y_ref, b, TOL, f"n=1024 set {i} M {M}")
+        one = host(kq.gemv(1, p, W.shape[0], K, dev(x), 1024, dev(s), split_k=1))
+        assert np.array_equal(y.view(np.uint32), one.view(np.uint32)), f"set {i} differs from its own call"
+    if M == 8:
+        K2 = 5120
+        p2 = [kq.pack(1, dev(inputs.weights(1499, 64, K2)))]
+        y2, buf2 = guarded_empty((8, 64))
+        y2.fill_(-1.0)
+        with pytest.raises(kq.KQError) as e:
+            kq.kq_gemv_multi(1, 1, p2, [64], K2, dev(inputs.activations(1498, 8, K2)), 8, 1024,
+                             None, [y2])
+        assert e.value.name == "KQ_EUNSUPPORTED"
+        assert np.all(host(y2) == -1.0)
+        check_guard(buf2, 8 * 64)
 
 
 def test_multi_gate_up_full_size_sampled():

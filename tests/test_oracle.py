@@ -182,6 +182,49 @@ def test_pq2_aos_to_planar_layout():
     assert np.array_equal(deq, oracle.unpack_pq2_aos(aos.reshape(-1), N, K))
 
 
+@pytest.mark.parametrize("fmt,N,K", [(1, 37, 5120), (1, 17, 17408), (2, 37, 5120),
+                                     (2, 17, 17408), (1, 16, 1152), (2, 33, 288)])
+def test_aos_to_planar_multi_tile_multi_chunk(fmt, N, K):
+    """The layout change at shapes with several 16-row tiles, several 8-block
+    scale chunks per tile and ragged tails in both (N % 16, blocks % 8), on
+    random AoS bytes so that every block is distinct and a swapped tile or
+    chunk order shows.  Two restatements of the layout check it: the numpy
+    reshape of tests/_golden.py and a per-block offset formula."""
+    g = 128 if fmt == 1 else 32
+    nb = K // g
+    aos = inputs.random_bytes(90 + N + K, N * nb * 34).reshape(N, nb, 34)
+    pl = oracle.aos_to_planar(fmt, aos, N, K)
+    nt, C = (N + 15) // 16, (nb + 7) // 8
+    d_off = G.d_offset(N, K, fmt)
+    assert pl.size == d_off + nt * C * 256
+    # numpy restatement: code rows and scale slots
+    codes = G.code_rows(pl, N, K, fmt).reshape(N, nb, 32)
+    assert np.array_equal(codes, aos[:, :, 2:])
+    sc, pad = G.scale_bytes(pl, N, K, fmt)
+    assert np.array_equal(sc, aos[:, :, :2])
+    assert not pad.any()
+    # per-block offsets: tile (n // 16, b) at 512 (t nb + b), row n % 16 at 32 (n % 16);
+    # scale chunk (n // 16, b // 8) at d_off + 256 (t C + b // 8), row at 16 (n % 16), slot 2 (b % 8)
+    for n in range(N):
+        for b in range(nb):
+            t = n // 16
+            q0 = 512 * (t * nb + b) + 32 * (n % 16)
+            assert np.array_equal(pl[q0:q0 + 32], aos[n, b, 2:]), (n, b)
+            d0 = d_off + 256 * (t * C + b // 8) + 16 * (n % 16) + 2 * (b % 8)
+            assert np.array_equal(pl[d0:d0 + 2], aos[n, b, :2]), (n, b)
+    # everything else (code rows past N, scale slots past N or nb, the gap
+    # before the scale plane) is zero
+    used = np.zeros(pl.size, bool)
+    for n in range(N):
+        for b in range(nb):
+            t = n // 16
+            q0 = 512 * (t * nb + b) + 32 * (n % 16)
+            used[q0:q0 + 32] = True
+            d0 = d_off + 256 * (t * C + b // 8) + 16 * (n % 16) + 2 * (b % 8)
+            used[d0:d0 + 2] = True
+    assert not pl[~used].any()
+
+
 # --------------------------------------------------------------------------
 # Q8_0 format
 # --------------------------------------------------------------------------
