@@ -3,19 +3,32 @@
 Headline workload: PQ2_0 GEMV, K=5120, N=10240, M=1 (the fused-QKV shape of
 the Bonsai 27B decoder), activation rotated by a blockwise Walsh-Hadamard
 transform with block 128.  One step = one kq_gemv call over one activation
-vector: a single kernel launch whose prologue rotates x in LDS before the
-GEMV; inputs are resident in HBM.  40 distinct
-packed weight copies (557 MB > 2 x 256 MB MALL) are used in turn so that every
-step streams its weights from HBM rather than from the Infinity Cache.  The
-timed loop replays a captured HIP graph of 40 steps (launch-bound inner loop);
-eager-launch timing is reported beside it.
+vector: a single kernel launch (the rotation runs in its prologue), inputs
+resident in HBM.  Steps use 40 distinct packed weight copies in turn (557 MB,
+more than twice the 256 MB last-level cache), so every step streams its
+weights from HBM.  Steps are replayed from captured HIP graphs (the decode
+inner loop is launch-bound); the timed region is exactly --steps steps,
+between two stream synchronisations, repeated for several samples; the line
+reports the median sample and its median absolute deviation (MAD).
 
-Prints ONE JSON line.  `value` = streamed weight bytes per step / step time.
-`roofline` is for the dominant kernel (the fused GEMV, the only launch of a
-step, timed with HIP events on its stream); `cpu_baseline` times the C oracle on the host cores.
+In the same session, on the same GPU:
+* walls: a >= 2 GiB streaming read-reduce (the reachable HBM read rate) and
+  the same read at the GEMV's size over the same rotating copies;
+* the GEMV's loads-only twin (same grid, same loads, no arithmetic);
+* the other configurations (Q8_0 M = 1/4/8, the 248320-row head with
+  split-K 1/2/4, the gate|up pair in one launch, the prefill GEMM, the
+  rotation pre-pass);
+* cpu_baseline: the CPU oracle, as it stands, on the host cores.
+
+Prints ONE JSON line.  `value` = streamed weight bytes per step / median step
+time.  `roofline` is for the dominant kernel, the fused GEMV (the only launch
+of a step): algorithmic bytes (weights + x + y) per launch / the median time
+per launch measured with HIP events on the stream it is launched on.
 """
 import argparse
+import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -32,73 +45,158 @@ def gbs(nbytes, seconds):
     return nbytes / seconds / 1e9
 
 
-def time_graph(fn_list, replays, warmup, stream):
-    """Capture fn_list (closures that enqueue work) as one graph, replay it
-    `replays` times; returns seconds per replay (HIP events on `stream`)."""
-    import torch
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        for f in fn_list:        # warm the code paths before capture
-            f()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=stream):
-        for f in fn_list:
-            f()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):      # replay() launches on the current stream
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(replays):
-            g.replay()
-        e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / replays, g
+def median_mad(xs):
+    s = sorted(xs)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    dev = sorted(abs(x - med) for x in xs)
+    mad = dev[n // 2] if n % 2 else 0.5 * (dev[n // 2 - 1] + dev[n // 2])
+    return med, mad
 
 
-def time_eager(fn_list, reps, stream):
-    import torch
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        for f in fn_list:
-            f()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            for f in fn_list:
+class StepGraphs:
+    """Steps i = 0, 1, 2, ... run fns[i % L]; k steps are replayed from a
+    captured graph of L steps (k // L times) and one of the first k % L."""
+
+    def __init__(self, fns, stream):
+        import torch
+        self.fns, self.stream, self.graphs = fns, stream, {}
+        with torch.cuda.stream(stream):
+            for f in fns:             # warm the code paths before capture
                 f()
-        e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / (reps * len(fn_list))
+        torch.cuda.synchronize()
+
+    def _graph(self, n):
+        import torch
+        if n not in self.graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                for f in self.fns[:n]:
+                    f()
+            self.graphs[n] = g
+        return self.graphs[n]
+
+    def run(self, k):
+        import torch
+        L = len(self.fns)
+        q, r = divmod(k, L)
+        with torch.cuda.stream(self.stream):    # replay() launches on the current stream
+            for _ in range(q):
+                self._graph(L).replay()
+            if r:
+                self._graph(r).replay()
+
+    def time(self, steps, warmup, samples):
+        """Seconds per step: median and MAD over `samples` timed regions of
+        exactly `steps` steps, each between two synchronisations."""
+        import torch
+        if warmup:
+            self.run(warmup)
+        self._graph(len(self.fns))
+        if steps % len(self.fns):
+            self._graph(steps % len(self.fns))
+        per = []
+        for _ in range(samples):
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            self.run(steps)
+            e1.record(self.stream)
+            e1.synchronize()
+            per.append(e0.elapsed_time(e1) / 1e3 / steps)
+        torch.cuda.synchronize()
+        return median_mad(per)
 
 
-def cpu_baseline(W, x, N, K, n, budget_s=10.0):
-    """The oracle as it stands (unpack, explicit-matrix rotation, binary64
-    product), on the host cores, over whole C2 calls until ~budget_s."""
-    import oracle
-    aos = oracle.pack_pq2_aos(W)
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        oracle.gemv_aos(oracle.FMT_PQ2_0, aos, N, K, x, n)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per_call = el / calls
-    return {"value": round(gbs(N * K // 128 * 34, per_call), 4), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{calls} full K=5120 N=10240 M=1 calls (unpack + rotate + fp64 product), "
-                      f"{per_call * 1e3:.1f} ms per call"}
+def time_fns(fns, stream, steps=None, samples=5):
+    """Median seconds per call of a list of closures (one per weight copy)."""
+    sg = StepGraphs(fns, stream)
+    steps = steps or max(len(fns), 20)
+    med, mad = sg.time(steps, len(fns), samples)
+    return med, mad
 
 
-def extras(kq, inputs, stream, quick):
+def source_sha(*names):
+    h = hashlib.sha256()
+    for f in names:
+        with open(os.path.join(ROOT, "gemm_kq_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profile_fields(fname, sha):
+    """key: value fields of a committed profile summary, or None when the
+    kernel source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    return fields if fields.get("kernel_source_sha") == sha else None
+
+
+def gemv_sha():
+    return source_sha("gemv.hip", "kq_device.h")
+
+
+def gemm_sha():
+    return source_sha("gemm.hip", "kq_device.h")
+
+
+# ---------------------------------------------------------------------------
+
+def walls(kq, copies, nbytes, stream):
+    """Reachable read rates: a 2 GiB streaming read, and a read of `nbytes`
+    (the GEMV's weights) over the same rotating copies."""
+    import torch
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = {}
+    big = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    best = None
+    for grid, block in ((1024, 512), (2048, 256), (2048, 512), (4096, 256)):
+        fns = [lambda g=grid, b=block: kq.kq_probe_read(big, big.numel(), 0, g, b, sink)]
+        t, mad = time_fns(fns, stream, steps=4, samples=5)
+        if best is None or t < best[0]:
+            best = (t, mad, grid, block)
+    t, mad, grid, block = best
+    out["read_2GiB"] = {"GBs": round(gbs(big.numel(), t), 1), "us": round(t * 1e6, 2),
+                        "mad_us": round(mad * 1e6, 2), "grid": grid, "block": block,
+                        "layout": "grid-stride, 16-byte non-temporal loads"}
+    del big
+    torch.cuda.empty_cache()
+    n16 = nbytes // 16 * 16
+    best = None
+    for layout, grid, block in ((0, 1024, 512), (0, 2048, 256), (0, 2048, 512), (0, 4096, 256),
+                                (1, 256, 640)):
+        fns = [lambda c=c, g=grid, b=block, l=layout: kq.kq_probe_read(c, n16, l, g, b, sink)
+               for c in copies]
+        t, mad = time_fns(fns, stream, steps=400, samples=5)
+        key = f"read_{nbytes / 1e6:.1f}MB_" + ("chunked_256x640" if layout else "grid_stride")
+        if layout == 0:
+            if best is None or t < best[0]:
+                best = (t, mad, grid, block)
+        else:
+            out[key] = {"GBs": round(gbs(n16, t), 1), "us": round(t * 1e6, 3),
+                        "mad_us": round(mad * 1e6, 3)}
+    t, mad, grid, block = best
+    out[f"read_{nbytes / 1e6:.1f}MB_grid_stride"] = {
+        "GBs": round(gbs(n16, t), 1), "us": round(t * 1e6, 3), "mad_us": round(mad * 1e6, 3),
+        "grid": grid, "block": block}
+    return out, t
+
+
+def extras(kq, inputs, stream):
     """Throughput of the other configurations (reported, not the headline)."""
     import numpy as np
     import torch
     out = {}
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     # Q8_0 GEMV K=5120 N=17408, M in {1,4,8}
     N, K = 17408, 5120
     W = torch.from_numpy(inputs.weights(1004, N, K)).cuda()
@@ -112,11 +210,15 @@ def extras(kq, inputs, stream, quick):
         y = torch.empty((M, N), device="cuda")
         fns = [(lambda c=c: kq.kq_gemv(kq.KQ_FMT_Q8_0, c, N, K, x, M, 0, None, 0, y, ws, nws))
                for c in copies]
-        t, _ = time_graph(fns, 20, 3, stream)
-        t /= len(fns)
+        t, mad = time_fns(fns, stream, steps=120)
+        fns = [(lambda c=c: kq.kq_probe_gemv_loads(kq.KQ_FMT_Q8_0, c, N, K, x, M, 0, 0, sink))
+               for c in copies]
+        tw, _ = time_fns(fns, stream, steps=120)
         out[f"q8_gemv_k5120_n17408_m{M}"] = {
-            "us_per_call": round(t * 1e6, 3), "weight_GBs": round(gbs(wbytes, t), 1),
-            "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4)}
+            "us_per_call": round(t * 1e6, 3), "mad_us": round(mad * 1e6, 3),
+            "weight_GBs": round(gbs(wbytes, t), 1),
+            "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4),
+            "us_loads_only_twin": round(tw * 1e6, 3)}
     del copies, p8
     # PQ2_0 gate|up: two 17408 x 5120 sets sharing one activation, one launch
     # (kq_gemv_multi) against two one-set launches
@@ -132,19 +234,18 @@ def extras(kq, inputs, stream, quick):
     wbytes = 2 * N * K // 128 * 34
     fns = [(lambda c=c: kq.kq_gemv_multi(kq.KQ_FMT_PQ2_0, 2, c, [N, N], K, x, 1, 128, None, ys))
            for c in pairs]
-    t, _ = time_graph(fns, 20, 3, stream)
-    t /= len(fns)
+    t, mad = time_fns(fns, stream, steps=120)
     fns = [(lambda c=c: [kq.kq_gemv(kq.KQ_FMT_PQ2_0, c[i], N, K, x, 1, 128, None, 1, ys[i], None, 0)
                          for i in range(2)]) for c in pairs]
-    t2, _ = time_graph(fns, 20, 3, stream)
-    t2 /= len(fns)
+    t2, _ = time_fns(fns, stream, steps=120)
     out["pq2_gemv_multi_k5120_2x17408"] = {
-        "us_per_call": round(t * 1e6, 3), "weight_GBs": round(gbs(wbytes, t), 1),
+        "us_per_call": round(t * 1e6, 3), "mad_us": round(mad * 1e6, 3),
+        "weight_GBs": round(gbs(wbytes, t), 1),
         "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4),
         "us_two_single_calls": round(t2 * 1e6, 3)}
     del pairs, sets
     torch.cuda.empty_cache()
-    # PQ2_0 lm_head GEMV K=5120 N=248320 (split-K 1, 2, 4)
+    # PQ2_0 output head K=5120 N=248320 (split-K 1, 2, 4, and the library's choice)
     N = 248320
     W = torch.from_numpy(inputs.weights(1003, N, K)).cuda()
     ph = kq.pack(kq.KQ_FMT_PQ2_0, W)
@@ -153,16 +254,21 @@ def extras(kq, inputs, stream, quick):
     heads = [ph, ph.clone()]
     x = torch.from_numpy(inputs.activations(2003, 1, K)).cuda()
     wbytes = N * K // 128 * 34
-    for S in (1, 2, 4):
+    abytes = wbytes + K * 4 + N * 4
+    for S in (1, 2, 4, 0):
         ws, nws = kq.workspace(0, kq.KQ_FMT_PQ2_0, 1, N, K, 128, S)
         y = torch.empty((1, N), device="cuda")
         fns = [(lambda c=c: kq.kq_gemv(kq.KQ_FMT_PQ2_0, c, N, K, x, 1, 128, None, S, y, ws, nws))
                for c in heads]
-        t, _ = time_graph(fns, 10, 2, stream)
-        t /= len(fns)
-        out[f"pq2_gemv_k5120_n248320_split{S}"] = {
-            "us_per_call": round(t * 1e6, 2), "weight_GBs": round(gbs(wbytes, t), 1),
-            "frac_hbm_peak": round(gbs(wbytes, t) / HBM_PEAK_GBS, 4)}
+        t, mad = time_fns(fns, stream, steps=40)
+        fns = [(lambda c=c: kq.kq_probe_gemv_loads(kq.KQ_FMT_PQ2_0, c, N, K, x, 1, 128, S, sink))
+               for c in heads]
+        tw, _ = time_fns(fns, stream, steps=40)
+        out[f"pq2_gemv_k5120_n248320_split{S if S else 'auto'}"] = {
+            "us_per_call": round(t * 1e6, 2), "mad_us": round(mad * 1e6, 3),
+            "weight_GBs": round(gbs(wbytes, t), 1),
+            "frac_hbm_peak": round(gbs(abytes, t) / HBM_PEAK_GBS, 4),
+            "us_loads_only_twin": round(tw * 1e6, 2)}
     del heads, ph
     torch.cuda.empty_cache()
     # PQ2_0 prefill GEMM M=2048 K=5120 N=10240 (bf16 MFMA)
@@ -174,36 +280,107 @@ def extras(kq, inputs, stream, quick):
     ws, nws = kq.workspace(1, kq.KQ_FMT_PQ2_0, M, N, K, 128)
     y = torch.empty((M, N), device="cuda")
     fns = [lambda: kq.kq_gemm(kq.KQ_FMT_PQ2_0, pg, N, K, xb, kq.KQ_BF16, M, 128, None, y, ws, nws)]
-    t, _ = time_graph(fns, 20, 3, stream)
+    t, mad = time_fns(fns, stream, steps=20)
     flops = 2.0 * M * N * K
-    out["pq2_gemm_m2048_k5120_n10240"] = {
-        "us_per_call": round(t * 1e6, 2), "TFLOPs": round(flops / t / 1e12, 1),
-        "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    # Hadamard pre-pass of the GEMM input, bf16 -> bf16
+    g = {"us_per_call": round(t * 1e6, 2), "mad_us": round(mad * 1e6, 3),
+         "TFLOPs": round(flops / t / 1e12, 1),
+         "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    counters = profile_fields("gemm_pq2_m2048_k5120_n10240_counters.txt", gemm_sha())
+    if counters:
+        g["mfma_util_rocprof"] = float(counters["mfma_util"])
+        g["lds_bank_conflict_frac_rocprof"] = float(counters.get("lds_bank_conflict_frac", "nan"))
+    out["pq2_gemm_m2048_k5120_n10240"] = g
+    # rotation pre-pass of the GEMM input, bf16 -> bf16
     xr = torch.empty_like(xb)
     fns = [lambda: kq.kq_hadamard_blocks(xb, kq.KQ_BF16, xr, kq.KQ_BF16, M, K, 128, None)]
-    t, _ = time_graph(fns, 50, 3, stream)
+    t, mad = time_fns(fns, stream, steps=40)
     out["hadamard_bf16_m2048_k5120"] = {"us_per_call": round(t * 1e6, 2),
                                         "GBs": round(gbs(2 * 2 * M * K, t), 1)}
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, x, N, K, n, inputs, budget_s=12.0):
+    """The oracle as it stands (unpack, explicit-matrix rotation, binary64
+    product) on the host cores: whole C2 calls on all threads until about half
+    the budget, one C2 call and one Q8_0 M=1 call on one thread, the Q8_0
+    call on all threads, and the PQ2_0 packer over the C2 weights."""
+    import numpy as np
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_num_threads(threads)
+    t0 = time.perf_counter()
+    aos = oracle.pack_pq2_aos(W)
+    t_pack = time.perf_counter() - t0
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemv_aos(oracle.FMT_PQ2_0, aos, N, K, x, n)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s / 2:
+            break
+    per_call = el / calls
+    Nq = 17408
+    Wq = inputs.weights(1004, Nq, K)
+    xq = inputs.activations(2004, 1, K)
+    aq = oracle.pack_q8_aos(Wq)
+    t0 = time.perf_counter()
+    oracle.gemv_aos(oracle.FMT_Q8_0, aq, Nq, K, xq, 0)
+    t_q8 = time.perf_counter() - t0
+    oracle.set_num_threads(1)
+    t0 = time.perf_counter()
+    oracle.gemv_aos(oracle.FMT_PQ2_0, aos, N, K, x, n)
+    t_c2_1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gemv_aos(oracle.FMT_Q8_0, aq, Nq, K, xq, 0)
+    t_q8_1 = time.perf_counter() - t0
+    oracle.set_num_threads(threads)
+    wb = N * K // 128 * 34
+    return {"value": round(gbs(wb, per_call), 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} whole K=5120 N=10240 M=1 PQ2_0 calls (unpack + explicit-matrix "
+                      f"rotation + binary64 product) on {threads} threads, "
+                      f"{per_call * 1e3:.1f} ms per call",
+            "cpu_model": cpu_model(),
+            "pq2_k5120_n10240_ms_per_call": round(per_call * 1e3, 2),
+            "pq2_k5120_n10240_ms_1thread": round(t_c2_1 * 1e3, 1),
+            "q8_k5120_n17408_m1_ms_per_call": round(t_q8 * 1e3, 2),
+            "q8_k5120_n17408_m1_ms_1thread": round(t_q8_1 * 1e3, 1),
+            "q8_k5120_n17408_m1_GBs": round(gbs(Nq * K // 32 * 34, t_q8), 4),
+            "pack_pq2_k5120_n10240_ms": round(t_pack * 1e3, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4000)
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--samples", type=int, default=7,
+                    help="timed regions of --steps steps (more when --steps is small)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-walls", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the single-GPU kernel is the measured unit; see DESIGN.md for how it would shard)",
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the measured unit "
+              "is the single-GPU kernel at its real shape; DESIGN.md says how it would shard)",
               file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
-    import numpy as np
     import torch
 
     import gemm_kq_gemv_amd as kq
@@ -221,92 +398,73 @@ def main():
     y = torch.empty((M, N), device="cuda")
     weight_bytes = N * K // 128 * 34
     algo_bytes = weight_bytes + M * K * 4 + M * N * 4
-
-    def step(c):
-        return lambda: kq.kq_gemv(kq.KQ_FMT_PQ2_0, c, N, K, x, M, n, None, 1, y, ws, nws)
-
-    steps = [step(c) for c in copies]
-    replays = max(1, args.steps // len(steps))
-    warm = max(1, args.warmup // len(steps))
-    n_steps = replays * len(steps)
     torch.cuda.synchronize()
-    t_rep, graph = time_graph(steps, replays, warm, stream)
-    t_step = t_rep / len(steps)
-    t_step_eager = time_eager(steps, max(1, replays // 4), stream)
 
-    # one step is one launch (the rotation runs in the GEMV prologue), so the
-    # dominant kernel's average launch duration is the graph-replayed step time;
-    # the standalone pre-pass kernel is timed for reference
-    t_kernel = t_step
+    samples = max(args.samples, min(200, math.ceil(20000 / args.steps)))
+    steps = StepGraphs([(lambda c=c: kq.kq_gemv(kq.KQ_FMT_PQ2_0, c, N, K, x, M, n, None, 1, y,
+                                                 ws, nws)) for c in copies], stream)
+    t_step, t_mad = steps.time(args.steps, args.warmup, samples)
+
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    twin = StepGraphs([(lambda c=c: kq.kq_probe_gemv_loads(kq.KQ_FMT_PQ2_0, c, N, K, x, M, n, 1,
+                                                            sink)) for c in copies], stream)
+    t_twin, t_twin_mad = twin.time(args.steps, args.warmup, samples)
     xr = torch.empty_like(x)
-    had_only = [lambda: kq.kq_hadamard_blocks(x, kq.KQ_F32, xr, kq.KQ_F32, M, K, n, None)]
-    t_h, _ = time_graph(had_only * len(steps), max(1, replays // 4), 2, stream)
-    t_had = t_h / len(steps)
+    had = StepGraphs([lambda: kq.kq_hadamard_blocks(x, kq.KQ_F32, xr, kq.KQ_F32, M, K, n, None)],
+                     stream)
+    t_had, _ = had.time(400, 40, 5)
 
-    traffic = measured_traffic()
-
+    traffic = profile_fields("gemv_pq2_k5120_n10240_traffic.txt", gemv_sha())
     value = gbs(weight_bytes, t_step)
+    achieved = gbs(algo_bytes, t_step)
     result = {
         "metric": "streamed weight GB/s and % of HBM peak, PQ2_0 GEMV K=5120 N=10240 batch 1",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": n_steps,
-        "warmup": warm * len(steps),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "samples": samples,
         "ms_per_step": round(t_step * 1e3, 6),
+        "mad_us_per_step": round(t_mad * 1e6, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp4(c-1)/2 x e5m2 (x' as 4 terms) -> f32",
         "data": "synthetic",
-        "config": {"workload": "PQ2_0 GEMV y = W (H_128 x), K=5120, N=10240, M=1, fp32 x/y; "
-                               "40 rotating packed weight copies; graph-replayed steps",
-                   "K": K, "N": N, "M": M, "block_len": n, "weight_bytes": weight_bytes},
+        "config": {"workload": "PQ2_0 GEMV y = W (H_128 x), K=5120, N=10240, M=1, fp32 x and y; "
+                               "seeded N(0,1) weights and activations; 40 rotating packed "
+                               "weight copies; graph-replayed steps",
+                   "K": K, "N": N, "M": M, "block_len": n, "weight_bytes": weight_bytes,
+                   "algorithmic_bytes": algo_bytes},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "gemv_calls_per_s": round(1.0 / t_step, 1),
-        "us_per_step_eager": round(t_step_eager * 1e6, 3),
-        "us_gemv_kernel": round(t_kernel * 1e6, 3),
-        "us_standalone_hadamard": round(t_had * 1e6, 3),
-        "roofline": {"bound": "hbm", "achieved": round(gbs(algo_bytes, t_kernel), 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs(algo_bytes, t_kernel) / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "us_per_step": round(t_step * 1e6, 3),
+        "us_loads_only_twin": round(t_twin * 1e6, 3),
+        "mad_us_loads_only_twin": round(t_twin_mad * 1e6, 4),
+        "us_standalone_hadamard_f32": round(t_had * 1e6, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": int(traffic["bytes_per_launch"]) if traffic else None,
+                     "kernel": "gemv_pq2_kernel<1,...> (one launch per step)",
+                     "time": "median HIP-event time per launch over the timed regions"},
     }
+    if not args.no_walls:
+        try:
+            w, t_wall = walls(kq, copies, weight_bytes, stream)
+            result["walls"] = w
+            result["frac_of_wall"] = round(t_wall / t_step, 4)
+            result["frac_of_loads_only_twin"] = round(t_twin / t_step, 4)
+        except Exception as e:  # the headline line must still print
+            result["walls"] = {"error": repr(e)}
     if not args.no_extras:
         try:
-            result["others"] = extras(kq, inputs, stream, False)
-        except Exception as e:  # the headline line must still print
+            result["others"] = extras(kq, inputs, stream)
+        except Exception as e:
             result["others"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(W_host, x_host, N, K, n, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(W_host, x_host, N, K, n, inputs, args.cpu_budget)
     print(json.dumps(result), flush=True)
-
-
-def measured_traffic():
-    """HBM bytes per launch from the committed PMC summary (FETCH_SIZE and
-    WRITE_SIZE, scaled by a plain copy), or None when the GEMV source has
-    changed since the counters were taken."""
-    tfile = os.path.join(ROOT, "profiles", "gemv_pq2_k5120_n10240_traffic.txt")
-    if not os.path.exists(tfile):
-        return None
-    fields = {}
-    with open(tfile) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return int(fields["bytes_per_launch"])
-
-
-def kernel_source_sha():
-    import hashlib
-    h = hashlib.sha256()
-    for f in ("gemv.hip", "kq_device.h"):
-        with open(os.path.join(ROOT, "gemm_kq_gemv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

@@ -32,10 +32,12 @@ KQ_OK = 0
 STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_EALIGN",
                 4: "KQ_EWORKSPACE", 5: "KQ_EUNSUPPORTED", 6: "KQ_EDEVICE"}
 
-# exported symbols, in include/kq.h order
+# exported symbols, in include/kq.h order, then the measurement instruments of
+# include/kq_probe.h
 EXPORTS = ("kq_status_string", "kq_packed_bytes", "kq_pack_pq2", "kq_pack_q8",
            "kq_unpack", "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv",
            "kq_gemv_multi", "kq_gemm")
+PROBE_EXPORTS = ("kq_probe_read", "kq_probe_gemv_loads")
 MAX_SETS = 4
 
 _p = C.c_void_p
@@ -63,6 +65,10 @@ _lib.kq_gemv_multi.argtypes = [C.c_int, _i32, C.POINTER(_p), C.POINTER(_i64), _i
 _lib.kq_gemm.restype = C.c_int
 _lib.kq_gemm.argtypes = [C.c_int, _p, _i64, _i64, _p, C.c_int, _i64, _i32, _p, _p, _p,
                          C.c_size_t, _p]
+_lib.kq_probe_read.restype = C.c_int
+_lib.kq_probe_read.argtypes = [_p, C.c_size_t, _i32, _i32, _i32, _p, _p]
+_lib.kq_probe_gemv_loads.restype = C.c_int
+_lib.kq_probe_gemv_loads.argtypes = [C.c_int, _p, _i64, _i64, _p, _i64, _i32, _i32, _p, _p]
 
 
 class KQError(RuntimeError):
@@ -157,6 +163,17 @@ def kq_gemm(fmt: int, packed, N: int, K: int, x, x_dt: int, M: int, block_len: i
             signs, y, workspace, ws_bytes: int, stream=None):
     _check(_lib.kq_gemm(fmt, _ptr(packed), N, K, _ptr(x), x_dt, M, block_len, _ptr(signs),
                         _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)), "kq_gemm")
+
+
+def kq_probe_read(buf, nbytes: int, layout: int, grid: int, block: int, sink, stream=None):
+    _check(_lib.kq_probe_read(_ptr(buf), nbytes, layout, grid, block, _ptr(sink),
+                              _stream(stream)), "kq_probe_read")
+
+
+def kq_probe_gemv_loads(fmt: int, packed, N: int, K: int, x, M: int, block_len: int,
+                        split_k: int, sink, stream=None):
+    _check(_lib.kq_probe_gemv_loads(fmt, _ptr(packed), N, K, _ptr(x), M, block_len, split_k,
+                                    _ptr(sink), _stream(stream)), "kq_probe_gemv_loads")
 
 
 # ---- allocation conveniences (torch.empty + one call above) -----------------

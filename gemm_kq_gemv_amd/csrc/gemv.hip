@@ -315,6 +315,53 @@ __device__ __forceinline__ void reduce_round(const WgRows& a, const float* part,
 }
 
 // ---------------------------------------------------------------------------
+// Weight loads of one row block for one wave (shared by every GEMV kernel and
+// by its loads-only twin): the codes of the wave's GS groups, one 16-byte
+// streamed load per lane and pair of groups, and the GS fp16 scales of the
+// lane's row.  ro / rod: byte offsets of the row block in the code and scale
+// resources (kFarRows past the workgroup's range, which returns zeros).
+
+template <int GS>
+struct WBuf {
+  uint4 q[GS / 2];
+  uint32_t d[GS / 2];
+};
+
+// qoff: per pair, the lane's code offset inside a row block (or kOutOfRange);
+// doff: the lane's offset of its first scale inside a 16-row scale tile;
+// gfirst: absolute index of the wave's first group; DALIGN: gfirst % 8 == 0
+// for GS >= 8, gfirst % 4 == 0 for GS == 4 (whole aligned runs of scales).
+template <int GS, bool DALIGN>
+__device__ __forceinline__ void issue_row_block(WBuf<GS>& b, BufRsrc rq, BufRsrc rd,
+                                                const uint32_t (&qoff)[GS / 2], uint32_t doff,
+                                                int gfirst, int r16, uint32_t ro, uint32_t rod) {
+#pragma unroll
+  for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
+  if constexpr (DALIGN) {
+    if constexpr (GS == 4) {
+      const uint2 t = buffer_load_8B(rd, doff + rod);
+      b.d[0] = t.x; b.d[1] = t.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < GS / 8; ++i) {
+        const uint4 t = buffer_load_16B(rd, doff + rod + 256u * i);
+        b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
+      }
+    }
+  } else {
+    // one scale per load, each at its own chunk and slot
+    const uint32_t rbase = (uint32_t)r16 * 16u + rod;
+#pragma unroll
+    for (int i = 0; i < GS / 2; ++i) {
+      const int ge = gfirst + 2 * i, go = ge + 1;
+      const uint32_t oe = (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u;
+      const uint32_t oo = (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u;
+      b.d[i] = buffer_load_2B(rd, rbase + oe) | (buffer_load_2B(rd, rbase + oo) << 16);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // PQ2_0
 
 // EPL activation elements per lane in the prologue: 8 (half a packed code
@@ -474,45 +521,22 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   }
   // scales of row r16, group gw: chunk gw / 8 of the tile, row r16, slot gw % 8
   const uint32_t doff = (uint32_t)(gw >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gw & 7) * 2u;
-  struct WBuf {
-    uint4 q[GS / 2];
-    uint32_t d[GS / 2];
-  };
+  using WB = WBuf<GS>;
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   // scales: the workgroup's whole 16-row tiles of the scale plane (padding is zero)
   const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
-  auto issue = [&](int j, WBuf& b) {
+  auto issue = [&](int j, WB& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
-#pragma unroll
-    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
-    if (DALIGN) {  // gw % GS == 0: the GS scales are one aligned run of a chunk row
-      if constexpr (GS == 4) {
-        const uint2 t = buffer_load_8B(rd, doff + rod);
-        b.d[0] = t.x; b.d[1] = t.y;
-      } else {
-        const uint4 t = buffer_load_16B(rd, doff + rod);
-        b.d[0] = t.x; b.d[1] = t.y; b.d[2] = t.z; b.d[3] = t.w;
-      }
-    } else {
-      // one scale per load, each at its own chunk and slot
-#pragma unroll
-      for (int i = 0; i < GS / 2; ++i) {
-        const int ge = gw + 2 * i, go = ge + 1;
-        const uint32_t oe = (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u;
-        const uint32_t oo = (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u;
-        const uint32_t rbase = (uint32_t)r16 * 16u + rod;
-        b.d[i] = buffer_load_2B(rd, rbase + oe) | (buffer_load_2B(rd, rbase + oo) << 16);
-      }
-    }
+    issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gw, r16, ro, rod);
   };
   // Only the first row block is loaded before the prologue.  A wave stalls at a
   // load it cannot issue while the compute unit's memory pipeline is full, and
   // a stalled wave does no arithmetic; with all D blocks issued here the waves
   // sat through the fetch and rotated x only afterwards.
-  WBuf wb[D];
+  WB wb[D];
   issue(0, wb[0]);
 
   // ---- per-wave prologue: rotation, per-group range scale, e5m2 terms
@@ -642,7 +666,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 
   // ---- main loop over row blocks
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const WBuf& b, int j) {
+  auto compute = [&](const WB& b, int j) {
     uint2 wq[GS];
 #pragma unroll
     for (int q = 0; q < GS / 2; ++q) pair_to_operands(b.q[q], wq[2 * q], wq[2 * q + 1]);
@@ -854,7 +878,6 @@ template <int M, bool DALIGN, bool MULTI>
 __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a) {
   static_assert(M <= 4, "one operand tile: four digits of up to four activation rows");
   constexpr int GS = Q8Cfg<M>::GS, D = Q8Cfg<M>::D, RBR = Q8Cfg<M>::RBR;
-  constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
   constexpr int TILES = (M + 3) / 4;
   extern __shared__ __align__(16) uint8_t lds[];
 
@@ -914,43 +937,22 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   // scales of row r16, group gq = g0 + gw: chunk gq / 8 of the tile, row r16, slot gq % 8
   const int gq = g0 + gw;
   const uint32_t doff = (uint32_t)(gq >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gq & 7) * 2u;
-  struct WBuf {
-    uint4 q[GS / 2];
-    uint32_t d[DW];
-  };
+  using WB = WBuf<GS>;
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
-  auto issue = [&](int j, WBuf& b) {
+  auto issue = [&](int j, WB& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
-    const uint32_t dro = rod + doff;
-#pragma unroll
-    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
-    if (DALIGN) {  // gq % 8 == 0: GS / 8 whole chunk rows of 8 scales
-#pragma unroll
-      for (int i = 0; i < GS / 8; ++i) {
-        const uint4 t = buffer_load_16B(rd, dro + 256u * i);
-        b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
-      }
-    } else {
-      // one scale per load, each at its own chunk and slot
-#pragma unroll
-      for (int i = 0; i < DW; ++i) {
-        const int ge = gq + 2 * i, go = ge + 1;
-        const uint32_t rbase = (uint32_t)r16 * 16u + rod;
-        const uint32_t lo = buffer_load_2B(rd, rbase + (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u);
-        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, rbase + (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u) : 0u;
-        b.d[i] = lo | (hi << 16);
-      }
-    }
+    issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gq, r16, ro, rod);
   };
+
   // One row: only the first row block is requested before the prologue (a
   // wave stalls at a load it cannot issue while the memory pipeline is full,
   // and a stalled wave does no arithmetic); the rest after it.
   constexpr int DPRE = M == 1 ? 1 : D;
-  WBuf wb[D];
+  WB wb[D];
 #pragma unroll
   for (int i = 0; i < DPRE; ++i) issue(i, wb[i]);
 
@@ -1097,7 +1099,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   // ---- main loop over row blocks
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const i32x4 izero = {0, 0, 0, 0};
-  auto compute = [&](const WBuf& b, int j) {
+  auto compute = [&](const WB& b, int j) {
     float Y[TILES][4];
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -1163,7 +1165,6 @@ __host__ __device__ inline int q8b_lds_bytes(int M, int NW, int GS) {
 template <int M, bool DALIGN, bool MULTI>
 __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvArgs a) {
   constexpr int GS = Q8Cfg<M>::GS, D = Q8Cfg<M>::D, RBR = Q8Cfg<M>::RBR;
-  constexpr int DW = (GS + 1) / 2;  // dwords of fp16 scales per row block
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -1220,39 +1221,18 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
   // scales of row r16, group gq = g0 + gw: chunk gq / 8 of the tile, row r16, slot gq % 8
   const int gq = g0 + gw;
   const uint32_t doff = (uint32_t)(gq >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gq & 7) * 2u;
-  struct WBuf {
-    uint4 q[GS / 2];
-    uint32_t d[DW];
-  };
+  using WB = WBuf<GS>;
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
-  auto issue = [&](int j, WBuf& b) {
+  auto issue = [&](int j, WB& b) {
     const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
     const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
-    const uint32_t dro = rod + doff;
-#pragma unroll
-    for (int q = 0; q < GS / 2; ++q) b.q[q] = buffer_load_16B_stream(rq, qoff[q] + ro);
-    if (DALIGN) {  // gq % 8 == 0: GS / 8 whole chunk rows of 8 scales
-#pragma unroll
-      for (int i = 0; i < GS / 8; ++i) {
-        const uint4 t = buffer_load_16B(rd, dro + 256u * i);
-        b.d[4 * i] = t.x; b.d[4 * i + 1] = t.y; b.d[4 * i + 2] = t.z; b.d[4 * i + 3] = t.w;
-      }
-    } else {
-      // one scale per load, each at its own chunk and slot
-#pragma unroll
-      for (int i = 0; i < DW; ++i) {
-        const int ge = gq + 2 * i, go = ge + 1;
-        const uint32_t rbase = (uint32_t)r16 * 16u + rod;
-        const uint32_t lo = buffer_load_2B(rd, rbase + (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u);
-        const uint32_t hi = 2 * i + 1 < GS ? buffer_load_2B(rd, rbase + (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u) : 0u;
-        b.d[i] = lo | (hi << 16);
-      }
-    }
+    issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gq, r16, ro, rod);
   };
-  WBuf wb[D];
+
+  WB wb[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) issue(i, wb[i]);
 
@@ -1329,7 +1309,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
 
   // ---- main loop over row blocks
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const WBuf& b, int j) {
+  auto compute = [&](const WB& b, int j) {
     f32x4 Y = zero;
 #pragma unroll
     for (int q = 0; q < GS / 2; ++q) {
@@ -1371,6 +1351,82 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Loads-only twin of the GEMV kernels (a measurement instrument): the same
+// grid, workgroup shape, activation loads and weight loads per wave
+// (issue_row_block with the same offsets and the same number of row blocks in
+// flight), every loaded word XOR-ed into one register; no rotation, no matrix
+// products, no reduction.  sink[0] is written only if the XOR equals an
+// unlikely constant, so that no load can be dropped.
+
+template <bool PQ2, int GS, int D, bool DALIGN>
+__global__ __launch_bounds__(1024) void gemv_loads_twin_kernel(GemvArgs a, int M, uint32_t* sink) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, kb = lane >> 4;
+  int g0, g1;
+  slice_groups(a, blockIdx.y, g0, g1);
+  const int gw = g0 + wave * GS;            // first group of this wave
+  const int vg = min(max(g1 - gw, 0), GS);  // its real groups
+  const WgRows wr = wg_rows<false>(a);
+  const int rb0 = wr.rb0, nrb = wr.rb1 - wr.rb0;
+  uint32_t acc = 0;
+  // activations: the PQ2_0 kernel's lanes hold 2 GS consecutive elements of
+  // the wave's K-range, the Q8_0 kernel's threads 16 of the workgroup's slice
+  if constexpr (PQ2) {
+    constexpr int EPL = 2 * GS;
+    if (lane / (128 / EPL) < vg)
+      for (int m = 0; m < M; ++m) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)m * a.K + (int64_t)gw * 128) + (EPL / 4) * lane;
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i) {
+          const uint4 f = src[i];
+          acc ^= f.x ^ f.y ^ f.z ^ f.w;
+        }
+      }
+  } else {
+    if (tid < ((g1 - g0) * 32) >> 4)
+      for (int m = 0; m < M; ++m) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)m * a.K + (int64_t)g0 * 32) + 4 * tid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 f = src[i];
+          acc ^= f.x ^ f.y ^ f.z ^ f.w;
+        }
+      }
+  }
+  uint32_t qoff[GS / 2];
+#pragma unroll
+  for (int q = 0; q < GS / 2; ++q) {
+    const int grp = 2 * q + (kb >> 1);
+    qoff[q] = grp < vg ? (uint32_t)(gw + grp) * 512u + 32u * r16 + 16u * (kb & 1) : kOutOfRange;
+  }
+  const uint32_t doff = (uint32_t)(gw >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gw & 7) * 2u;
+  const BufRsrc rq = make_rsrc(wr.qs + (int64_t)rb0 * kRB * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
+  const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  auto issue = [&](int j, WBuf<GS>& b) {
+    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gw, r16, ro, rod);
+  };
+  WBuf<GS> wb[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue(i, wb[i]);
+  for (int j0 = 0; j0 < nrb; j0 += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int j = j0 + i;
+      if (j < nrb) {
+#pragma unroll
+        for (int q = 0; q < GS / 2; ++q) acc ^= wb[i].q[q].x ^ wb[i].q[q].y ^ wb[i].q[q].z ^ wb[i].q[q].w ^ wb[i].d[q];
+      }
+      issue(j + D, wb[i]);
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
 // y[i] = sum_{s < S} part[s][i], ascending s.
@@ -1642,6 +1698,48 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;
+}
+
+int launch_gemv_loads_twin(int fmt, const void* packed, int64_t N, int64_t K, const float* x,
+                           int64_t M, int block_len, int split_req, uint32_t* sink, hipStream_t st) {
+  GemvPlan p = plan_gemv(fmt, M, N, K, block_len, split_req);
+  if (p.split < 1) return -2;
+  PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
+  GemvArgs a;
+  common_args(a, fmt, p, K, x, block_len, nullptr);
+  a.qs = pv.qs;
+  a.dpl = pv.d;
+  a.N = N;
+  a.out = nullptr;
+  a.total_rb = p.total_rb;
+  a.grid_x = p.grid_x;
+  a.rb_base = p.total_rb / p.grid_x;
+  a.rb_rem = p.total_rb % p.grid_x;
+  const dim3 grid(p.grid_x, p.split), block(p.nw * 64);
+  const int m = (int)M;
+  if (fmt == kFmtPQ2) {
+    constexpr int D = Pq2Cfg<8>::D;
+    static_assert(Pq2Cfg<16>::D == D, "one depth for both prologue shapes");
+    if (p.epl == 8) {
+      if (p.dalign) hipLaunchKernelGGL((gemv_loads_twin_kernel<true, Pq2Cfg<8>::GS, D, true>), grid, block, 0, st, a, m, sink);
+      else hipLaunchKernelGGL((gemv_loads_twin_kernel<true, Pq2Cfg<8>::GS, D, false>), grid, block, 0, st, a, m, sink);
+    } else {
+      if (p.dalign) hipLaunchKernelGGL((gemv_loads_twin_kernel<true, Pq2Cfg<16>::GS, D, true>), grid, block, 0, st, a, m, sink);
+      else hipLaunchKernelGGL((gemv_loads_twin_kernel<true, Pq2Cfg<16>::GS, D, false>), grid, block, 0, st, a, m, sink);
+    }
+  } else {
+    constexpr int GS = Q8Cfg<1>::GS;
+    if (Q8Cfg<1>::D == 2 && (M == 1 || M > 4)) {
+      static_assert(Q8Cfg<1>::D == 2 && Q8Cfg<8>::D == 2, "two row blocks in flight for 1 and 5..8 rows");
+      if (p.dalign) hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS, 2, true>), grid, block, 0, st, a, m, sink);
+      else hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS, 2, false>), grid, block, 0, st, a, m, sink);
+    } else {
+      static_assert(Q8Cfg<2>::D == 1 && Q8Cfg<4>::D == 1, "one row block in flight for 2..4 rows");
+      if (p.dalign) hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS, 1, true>), grid, block, 0, st, a, m, sink);
+      else hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS, 1, false>), grid, block, 0, st, a, m, sink);
+    }
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace kq

@@ -75,6 +75,15 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
 // bytes) stays a 32-bit buffer range well below the out-of-range offset.
 constexpr int64_t kGemmMaxK = int64_t(1) << 21;
 bool gemm_shape_supported(int64_t M, int64_t N, int64_t K);
+// Loads-only twin of launch_gemv (same plan and weight loads, no arithmetic);
+// -2 when kq_gemv has no plan for the arguments.
+int launch_gemv_loads_twin(int fmt, const void* packed, int64_t N, int64_t K, const float* x,
+                           int64_t M, int block_len, int split_req, uint32_t* sink, hipStream_t st);
+// Streaming read of `bytes` (a multiple of 16) at buf: layout 0 grid-stride,
+// 1 one contiguous chunk per workgroup.
+int launch_probe_read(const void* buf, size_t bytes, int layout, int grid, int block,
+                      uint32_t* sink, hipStream_t st);
+
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
                              const void* signs_hint);
 int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_bf16, int64_t M,

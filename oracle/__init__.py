@@ -79,6 +79,8 @@ def lib():
                                    p, p, p]
         L.kqo_num_threads.restype = C.c_int
         L.kqo_num_threads.argtypes = []
+        L.kqo_set_num_threads.restype = None
+        L.kqo_set_num_threads.argtypes = [C.c_int]
         _lib = L
     return _lib
 
@@ -224,3 +226,7 @@ def gemv_aos(fmt: int, aos, N: int, K: int, x, block_len: int, signs=None):
 
 def num_threads() -> int:
     return int(lib().kqo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().kqo_set_num_threads(int(n))

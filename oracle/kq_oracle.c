@@ -397,6 +397,15 @@ int kqo_num_threads(void)
 #endif
 }
 
+void kqo_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int kqo_gemv_aos(int fmt, const uint8_t *aos, int64_t N, int64_t K,
                  const float *x, int64_t M, int32_t block_len,
                  const int8_t *signs, double *y, double *bnd)

@@ -111,8 +111,9 @@ int kqo_gemv_aos(int fmt, const uint8_t *aos, int64_t N, int64_t K,
                  const float *x, int64_t M, int32_t block_len,
                  const int8_t *signs, double *y, double *bnd);
 
-/* number of OpenMP threads kqo_matmul uses */
+/* number of OpenMP threads kqo_matmul uses; set it (n >= 1) */
 int kqo_num_threads(void);
+void kqo_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -19,15 +19,23 @@ def _lib():
     return kq
 
 
+def _declared(header):
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|kq_status)\s*(kq_\w+)\s*\(",
+                                 text, re.M)))
+
+
 def test_exports_match_header():
     kq = _lib()
-    text = open(HEADER).read()
-    declared = sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|kq_status)\s*(kq_\w+)\s*\(",
-                                     text, re.M)))
+    declared = _declared(HEADER)
     assert declared == sorted(kq.EXPORTS)
+    probes = _declared(os.path.join(ROOT, "include", "kq_probe.h"))
+    assert probes == sorted(kq.PROBE_EXPORTS)
     cdll = C.CDLL(kq.LIB_PATH)
-    for name in declared:
+    for name in declared + probes:
         assert hasattr(cdll, name), name
+    # every header under include/ is covered
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["kq.h", "kq_probe.h"]
 
 
 def test_status_strings():
@@ -159,6 +167,24 @@ def test_gemm_rejections():
     # 32-bit buffer ranges: K above 2^21, or more output tiles than an int holds
     assert _status(g, 1, FAKE, 64, (1 << 21) + 128, FAKE, 1, 4, 0, None, FAKE, FAKE, ws, 0) == "KQ_EUNSUPPORTED"
     assert _status(g, 1, FAKE, 1 << 32, 128, FAKE, 1, 1 << 32, 0, None, FAKE, FAKE, ws, 0) == "KQ_EUNSUPPORTED"
+
+
+@pytest.mark.usefixtures("nogpu")
+def test_probe_rejections():
+    kq = _lib()
+    r = kq.kq_probe_read
+    assert _status(r, None, 1024, 0, 256, 256, FAKE, 0) == "KQ_EINVAL"
+    assert _status(r, FAKE, 1024, 2, 256, 256, FAKE, 0) == "KQ_EINVAL"
+    assert _status(r, FAKE, 1024, 0, 0, 256, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(r, FAKE, 1024, 0, 256, 96, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(r, FAKE, 1000, 0, 256, 256, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(r, MISALIGNED, 1024, 0, 256, 256, FAKE, 0) == "KQ_EALIGN"
+    t = kq.kq_probe_gemv_loads
+    assert _status(t, 3, FAKE, 64, 128, FAKE, 1, 128, 0, FAKE, 0) == "KQ_EINVAL"
+    assert _status(t, 1, FAKE, 64, 192, FAKE, 1, 128, 0, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(t, 1, FAKE, 64, 128, FAKE, 9, 128, 0, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(t, 1, FAKE, 64, 128, FAKE, 1, 128, 0, MISALIGNED, 0) == "KQ_EALIGN"
+    assert _status(t, 1, FAKE, 64, 5120, FAKE, 1, 1024, 6, FAKE, 0) == "KQ_EUNSUPPORTED"
 
 
 @pytest.mark.usefixtures("nogpu")
