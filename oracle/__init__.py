@@ -64,6 +64,9 @@ def lib():
                      "kqo_unpack_pq2_aos_words", "kqo_unpack_q8_aos"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = [p, i64, i64, p]
+        for name in ("kqo_pq2_to_ptq1_aos", "kqo_ptq1_to_pq2_aos", "kqo_unpack_ptq1_aos"):
+            getattr(L, name).restype = C.c_int
+            getattr(L, name).argtypes = [p, i64, i64, p]
         L.kqo_planar_bytes.restype = i64
         L.kqo_planar_bytes.argtypes = [C.c_int, i64, i64]
         L.kqo_aos_to_planar.restype = C.c_int
@@ -144,6 +147,30 @@ def pack_q8_aos(W) -> np.ndarray:
     N, K = W.shape
     out = np.empty(N * (K // 32) * 34, dtype=np.uint8)
     _check(lib().kqo_pack_q8_aos(_ptr(W), N, K, _ptr(out)), "pack_q8")
+    return out
+
+
+def pq2_to_ptq1_aos(pq2, N: int, K: int) -> np.ndarray:
+    """PTQ1_0 blocks [N * K/128 * 28] holding the trits of PQ2_0 blocks
+    (Bonsai page sec. 3.2)."""
+    pq2 = np.ascontiguousarray(pq2, dtype=np.uint8)
+    out = np.empty(N * (K // 128) * 28, dtype=np.uint8)
+    _check(lib().kqo_pq2_to_ptq1_aos(_ptr(pq2), N, K, _ptr(out)), "pq2_to_ptq1")
+    return out
+
+
+def ptq1_to_pq2_aos(ptq1, N: int, K: int) -> np.ndarray:
+    """The lossless PTQ1_0 -> PQ2_0 transcode (Bonsai page sec. 3.2)."""
+    ptq1 = np.ascontiguousarray(ptq1, dtype=np.uint8)
+    out = np.empty(N * (K // 128) * 34, dtype=np.uint8)
+    _check(lib().kqo_ptq1_to_pq2_aos(_ptr(ptq1), N, K, _ptr(out)), "ptq1_to_pq2")
+    return out
+
+
+def unpack_ptq1_aos(ptq1, N: int, K: int) -> np.ndarray:
+    ptq1 = np.ascontiguousarray(ptq1, dtype=np.uint8)
+    out = np.empty((N, K), dtype=np.float64)
+    _check(lib().kqo_unpack_ptq1_aos(_ptr(ptq1), N, K, _ptr(out)), "unpack_ptq1")
     return out
 
 

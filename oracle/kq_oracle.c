@@ -303,6 +303,100 @@ int kqo_unpack_q8_aos(const uint8_t *aos, int64_t N, int64_t K, double *W)
 }
 
 /* ======================================================================== */
+/* PTQ1_0 [BT 3.2]: the 128 trits of a block (the same values 0, 1, 2 as the  */
+/* PQ2_0 codes, same scale) in 24 + 2 bytes of base-3 digits, then the fp16  */
+/* scale: 28 bytes.                                                          */
+/* ======================================================================== */
+
+/* Where element e of a block lives: trit byte (0..25) and trit position n.
+ *   elements   0..79:  byte e % 16 of qs[0..15],  n = e / 16  (5 trits a byte)
+ *   elements  80..119: byte 16 + (e - 80) % 8,    n = (e - 80) / 8
+ *   elements 120..127: qh byte (e - 120) % 2,      n = (e - 120) / 2 (4 trits) */
+static void ptq1_place(int e, int *byte, int *n)
+{
+    if (e < 80) { *byte = e % 16; *n = e / 16; }
+    else if (e < 120) { *byte = 16 + (e - 80) % 8; *n = (e - 80) / 8; }
+    else { *byte = 24 + (e - 120) % 2; *n = (e - 120) / 2; }
+}
+
+/* A byte holding trits t0..t4 (t0 most significant):
+ *   q = ceil(256 * (81 t0 + 27 t1 + 9 t2 + 3 t3 + t4) / 243).
+ * A qh byte holds four trits; it is read as five with t4 = 0. */
+static uint8_t ptq1_byte(const int t[5])
+{
+    int v = 81 * t[0] + 27 * t[1] + 9 * t[2] + 3 * t[3] + t[4];
+    return (uint8_t)((256 * v + 242) / 243);
+}
+
+/* Trit n of byte q: ((q * 3^n) mod 256) * 3 / 256, rounded down. */
+static int ptq1_trit(uint8_t q, int n)
+{
+    int p = 1;
+    for (int i = 0; i < n; ++i) p *= 3;
+    return (((int)q * p) & 0xFF) * 3 >> 8;
+}
+
+int kqo_pq2_to_ptq1_aos(const uint8_t *pq2, int64_t N, int64_t K, uint8_t *ptq1)
+{
+    if (N < 0 || K <= 0 || K % 128) return -1;
+    int64_t nblk = N * (K / 128);
+    for (int64_t b = 0; b < nblk; ++b) {
+        const uint8_t *in = pq2 + b * 34;
+        uint8_t *out = ptq1 + b * 28;
+        int t[26][5];
+        memset(t, 0, sizeof t);
+        for (int e = 0; e < 128; ++e) {
+            int c = (in[2 + e / 4] >> (2 * (e % 4))) & 3;   /* [BT 3.1] */
+            if (c == 3) return -1;                           /* not a trit */
+            int byte, n;
+            ptq1_place(e, &byte, &n);
+            t[byte][n] = c;
+        }
+        for (int i = 0; i < 26; ++i) out[i] = ptq1_byte(t[i]);
+        out[26] = in[0];                                     /* d, LAST here */
+        out[27] = in[1];
+    }
+    return 0;
+}
+
+int kqo_ptq1_to_pq2_aos(const uint8_t *ptq1, int64_t N, int64_t K, uint8_t *pq2)
+{
+    if (N < 0 || K <= 0 || K % 128) return -1;
+    int64_t nblk = N * (K / 128);
+    for (int64_t b = 0; b < nblk; ++b) {
+        const uint8_t *in = ptq1 + b * 28;
+        uint8_t *out = pq2 + b * 34;
+        memset(out, 0, 34);
+        out[0] = in[26];
+        out[1] = in[27];
+        for (int e = 0; e < 128; ++e) {
+            int byte, n;
+            ptq1_place(e, &byte, &n);
+            int c = ptq1_trit(in[byte], n);
+            out[2 + e / 4] |= (uint8_t)(c << (2 * (e % 4)));
+        }
+    }
+    return 0;
+}
+
+int kqo_unpack_ptq1_aos(const uint8_t *ptq1, int64_t N, int64_t K, double *W)
+{
+    if (N < 0 || K <= 0 || K % 128) return -1;
+    int64_t nb = K / 128;
+    for (int64_t r = 0; r < N; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = ptq1 + (r * nb + b) * 28;
+            double d = (double)kqo_f32_from_f16((uint16_t)(blk[26] | (blk[27] << 8)));
+            for (int e = 0; e < 128; ++e) {
+                int byte, n;
+                ptq1_place(e, &byte, &n);
+                W[r * K + b * 128 + e] = (double)(ptq1_trit(blk[byte], n) - 1) * d;
+            }
+        }
+    return 0;
+}
+
+/* ======================================================================== */
 /* Rotation.                                                                */
 /* ======================================================================== */
 

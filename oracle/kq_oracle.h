@@ -10,7 +10,8 @@
  * Sources (the web pages this project follows):
  *   [BT]  "Bonsai 2 27B -- ternary g128 + blockwise Hadamard: the packing
  *         contract for a Core AI port" (Core AI model zoo knowledge page):
- *         sec. 3.1 (PQ2_0 block, quantizer, word view), sec. 4.1 (rotation
+ *         sec. 3.1 (PQ2_0 block, quantizer, word view), sec. 3.2 (PTQ1_0
+ *         trit block and its element order), sec. 4.1 (rotation
  *         definition, blockwise application), sec. 4.2 (runtime order).
  *   [KA]  "Kipp architecture" page: "Weight quantization" (Q8_0: 32-weight
  *         blocks, fp16 scale, quantized against the fp16-rounded scale).
@@ -83,6 +84,21 @@ int kqo_aos_to_planar(int fmt, const uint8_t *aos, int64_t N, int64_t K,
 int kqo_unpack_pq2_aos(const uint8_t *aos, int64_t N, int64_t K, double *W);
 int kqo_unpack_pq2_aos_words(const uint8_t *aos, int64_t N, int64_t K, double *W);
 int kqo_unpack_q8_aos(const uint8_t *aos, int64_t N, int64_t K, double *W);
+
+/* ---- PTQ1_0 [BT 3.2] ----------------------------------------------------
+ * 128 trits t in {0,1,2} (the PQ2_0 code values, (t-1)*d) per block: 24 bytes
+ * of five trits (elements 0..79: element 16n + m is trit n of byte m; 80..119:
+ * element 80 + 8n + m is trit n of byte 16 + m), 2 bytes of four trits
+ * (element 120 + 2n + h is trit n of byte 24 + h), then fp16 d (little
+ * endian, last): 28 bytes.  A byte of trits t0..t4 (t0 most significant) is
+ * ceil(256 (81 t0 + 27 t1 + 9 t2 + 3 t3 + t4) / 243), a four-trit byte read
+ * as t4 = 0; trit n of byte q is ((q 3^n) mod 256) * 3 / 256 rounded down.
+ * pq2_to_ptq1: -1 if a PQ2_0 block holds code 3 (not a trit).  ptq1_to_pq2
+ * is the lossless transcode to PQ2_0 blocks that [BT 3.2] recommends at load
+ * time; every byte value decodes (to trits 0..2). */
+int kqo_pq2_to_ptq1_aos(const uint8_t *pq2, int64_t N, int64_t K, uint8_t *ptq1);
+int kqo_ptq1_to_pq2_aos(const uint8_t *ptq1, int64_t N, int64_t K, uint8_t *pq2);
+int kqo_unpack_ptq1_aos(const uint8_t *ptq1, int64_t N, int64_t K, double *W);
 
 /* ---- rotation [BT 4.1, 4.2] --------------------------------------------
  * H_n[r][c] = (-1)^popcount(r & c)  (Sylvester, natural order), n = 2^i.

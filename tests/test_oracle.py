@@ -467,3 +467,117 @@ def test_bad_shapes_rejected():
         oracle.rotate(np.zeros(96), 64)
     with pytest.raises(ValueError):
         oracle.hadamard_matrix(12)
+
+
+# --------------------------------------------------------------------------
+# PTQ1_0 (Bonsai page, sec. 3.2): base-3 trits, lossless transcode to PQ2_0
+# --------------------------------------------------------------------------
+
+def _pq2_block_with_codes(codes, d16=0x3C00):
+    """One PQ2_0 AoS block (34 bytes) from 128 codes, written with the byte
+    rule of sec. 3.1 (element j in byte j/4 at bits 2 (j % 4))."""
+    blk = np.zeros(34, np.uint8)
+    blk[0], blk[1] = d16 & 0xFF, d16 >> 8
+    for j, c in enumerate(codes):
+        blk[2 + j // 4] |= np.uint8(int(c) << (2 * (j % 4)))
+    return blk
+
+
+def test_ptq1_byte_values_fixture():
+    g = G.load("ptq1_block.txt")
+    tuples = [G.ints(t) for t in g["byte_trits"].split("|")]
+    want = G.ints(g["byte_q"])
+    for t, q in zip(tuples, want):
+        # byte 0 of the trit bytes holds elements 0, 16, 32, 48, 64 (n = 0..4)
+        codes = np.ones(128, np.int64)
+        for n in range(5):
+            codes[16 * n] = t[n]
+        p1 = oracle.pq2_to_ptq1_aos(_pq2_block_with_codes(codes), 1, 128)
+        assert int(p1[0]) == int(q), (t, q)
+
+
+def test_ptq1_element_placement_fixture():
+    g = G.load("ptq1_block.txt")
+    for tok in g["place"].split():
+        e, byte, n = (int(v) for v in tok.split(":"))
+        codes = np.ones(128, np.int64)
+        codes[e] = 2
+        p1 = oracle.pq2_to_ptq1_aos(_pq2_block_with_codes(codes), 1, 128)
+        # every other trit byte holds all-ones trits
+        ones5, ones4 = 128, 127            # 1 1 1 1 1 -> 128; 1 1 1 1 (0) -> 127
+        base = np.array([ones5] * 24 + [ones4] * 2)
+        changed = np.nonzero(p1[:26] != base)[0]
+        assert list(changed) == [byte], (e, changed)
+        # the changed trit is position n: digit n of floor(243 q / 256) in base 3
+        v = (243 * int(p1[byte])) >> 8
+        digits = [(v // 3 ** (4 - i)) % 3 for i in range(5)]
+        assert digits[n] == 2 and sum(d != 1 for d in digits[:4 if byte >= 24 else 5]) == 1
+
+
+def test_ptq1_worked_block_fixture():
+    g = G.load("ptq1_block.txt")
+    codes = np.ones(128, np.int64)
+    for tok in g["block_trits"].split()[1:]:
+        e, v = tok.split("=")
+        codes[int(e)] = int(v)
+    d16 = int(g["block_d16"], 16)
+    p1 = oracle.pq2_to_ptq1_aos(_pq2_block_with_codes(codes, d16), 1, 128)
+    assert np.array_equal(p1, G.hex_bytes(g["block_bytes"]))
+    deq = oracle.unpack_ptq1_aos(p1, 1, 128)[0]
+    assert np.array_equal(deq, (codes - 1) * 0.5)
+
+
+def test_ptq1_trit_rule_all_bytes_vs_base3_digits():
+    """The page's extraction rule ((q 3^n) mod 256) * 3 >> 8 read through the
+    oracle's transcode, for every byte value q, against the textbook base-3
+    digits of q / 256 (the first five are those of floor(243 q / 256))."""
+    for q in range(256):
+        blk = np.full(28, 128, np.uint8)
+        blk[0] = q                         # elements 0, 16, 32, 48, 64
+        blk[24] = q                        # elements 120, 122, 124, 126
+        blk[26], blk[27] = 0x00, 0x3C
+        pq2 = oracle.ptq1_to_pq2_aos(blk, 1, 128)
+        codes = np.array([(pq2[2 + j // 4] >> (2 * (j % 4))) & 3 for j in range(128)])
+        v = (243 * q) >> 8
+        digits = [(v // 3 ** (4 - i)) % 3 for i in range(5)]
+        assert [int(codes[16 * n]) for n in range(5)] == digits, q
+        assert [int(codes[120 + 2 * n]) for n in range(4)] == digits[:4], q
+        # all other elements: byte 128 = trits 1 1 1 1 1
+        others = np.ones(128, bool)
+        others[[0, 16, 32, 48, 64, 120, 122, 124, 126]] = False
+        assert np.all(codes[others] == 1)
+        assert pq2[0] == 0x00 and pq2[1] == 0x3C
+
+
+def test_ptq1_every_tuple_round_trips():
+    """All 3^5 trit tuples of a five-trit byte and 3^4 of a qh byte survive
+    encode then decode."""
+    import itertools
+    for t in itertools.product(range(3), repeat=5):
+        codes = np.ones(128, np.int64)
+        for n in range(5):
+            codes[16 * n + 3] = t[n]       # byte 3
+        for n in range(4):
+            codes[120 + 2 * n + 1] = t[n]  # qh byte 1
+        blk = _pq2_block_with_codes(codes)
+        p1 = oracle.pq2_to_ptq1_aos(blk, 1, 128)
+        assert np.array_equal(oracle.ptq1_to_pq2_aos(p1, 1, 128), blk), t
+
+
+def test_ptq1_transcode_gaussian_lossless():
+    N, K = 37, 640
+    W = inputs.weights(31, N, K)
+    aos = oracle.pack_pq2_aos(W)
+    p1 = oracle.pq2_to_ptq1_aos(aos, N, K)
+    assert p1.size == N * (K // 128) * 28           # 1.75 bits per weight
+    assert np.array_equal(oracle.ptq1_to_pq2_aos(p1, N, K), aos)
+    assert np.array_equal(oracle.unpack_ptq1_aos(p1, N, K), oracle.unpack_pq2_aos(aos, N, K))
+    # the scale is the last two bytes of each block
+    assert np.array_equal(p1.reshape(-1, 28)[:, 26:], aos.reshape(-1, 34)[:, :2])
+
+
+def test_ptq1_rejects_code_3():
+    codes = np.ones(128, np.int64)
+    codes[5] = 3
+    with pytest.raises(ValueError):
+        oracle.pq2_to_ptq1_aos(_pq2_block_with_codes(codes), 1, 128)
