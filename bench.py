@@ -110,7 +110,10 @@ class StepGraphs:
 
 
 def time_fns(fns, stream, steps=None, samples=5):
-    """Median seconds per call of a list of closures (one per weight copy)."""
+    """Median seconds per call of a list of closures (one per weight copy),
+    repeated to at least 20 calls per graph so that short kernels are not
+    timed against the host's graph-launch rate."""
+    fns = fns * max(1, -(-20 // len(fns)))
     sg = StepGraphs(fns, stream)
     steps = steps or max(len(fns), 20)
     med, mad = sg.time(steps, len(fns), samples)
@@ -410,8 +413,8 @@ def main():
                                                             sink)) for c in copies], stream)
     t_twin, t_twin_mad = twin.time(args.steps, args.warmup, samples)
     xr = torch.empty_like(x)
-    had = StepGraphs([lambda: kq.kq_hadamard_blocks(x, kq.KQ_F32, xr, kq.KQ_F32, M, K, n, None)],
-                     stream)
+    had = StepGraphs([lambda: kq.kq_hadamard_blocks(x, kq.KQ_F32, xr, kq.KQ_F32, M, K, n, None)]
+                     * N_COPIES, stream)
     t_had, _ = had.time(400, 40, 5)
 
     traffic = profile_fields("gemv_pq2_k5120_n10240_traffic.txt", gemv_sha())

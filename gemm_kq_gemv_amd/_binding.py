@@ -35,7 +35,7 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_EALIGN",
 # exported symbols, in include/kq.h order, then the measurement instruments of
 # include/kq_probe.h
 EXPORTS = ("kq_status_string", "kq_packed_bytes", "kq_pack_pq2", "kq_pack_q8",
-           "kq_unpack", "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv",
+           "kq_transcode_ptq1", "kq_unpack", "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv",
            "kq_gemv_multi", "kq_gemm")
 PROBE_EXPORTS = ("kq_probe_read", "kq_probe_gemv_loads")
 MAX_SETS = 4
@@ -50,6 +50,8 @@ _lib.kq_packed_bytes.argtypes = [C.c_int, _i64, _i64]
 for _n in ("kq_pack_pq2", "kq_pack_q8"):
     getattr(_lib, _n).restype = C.c_int
     getattr(_lib, _n).argtypes = [_p, _i64, _i64, _p, _p]
+_lib.kq_transcode_ptq1.restype = C.c_int
+_lib.kq_transcode_ptq1.argtypes = [_p, _i64, _i64, _p, _p]
 _lib.kq_unpack.restype = C.c_int
 _lib.kq_unpack.argtypes = [C.c_int, _p, _i64, _i64, _p, _p]
 _lib.kq_hadamard_blocks.restype = C.c_int
@@ -127,6 +129,11 @@ def kq_pack_q8(W, N: int, K: int, packed, stream=None):
     _check(_lib.kq_pack_q8(_ptr(W), N, K, _ptr(packed), _stream(stream)), "kq_pack_q8")
 
 
+def kq_transcode_ptq1(ptq1, N: int, K: int, packed, stream=None):
+    _check(_lib.kq_transcode_ptq1(_ptr(ptq1), N, K, _ptr(packed), _stream(stream)),
+           "kq_transcode_ptq1")
+
+
 def kq_unpack(fmt: int, packed, N: int, K: int, W_out, stream=None):
     _check(_lib.kq_unpack(fmt, _ptr(packed), N, K, _ptr(W_out), _stream(stream)), "kq_unpack")
 
@@ -184,6 +191,14 @@ def pack(fmt: int, W, stream=None):
     N, K = W.shape
     out = torch.empty(kq_packed_bytes(fmt, N, K), dtype=torch.uint8, device=W.device)
     (kq_pack_pq2 if fmt == KQ_FMT_PQ2_0 else kq_pack_q8)(W, N, K, out, stream)
+    return out
+
+
+def transcode_ptq1(ptq1, N: int, K: int, stream=None):
+    """PTQ1_0 blocks (uint8 device tensor) -> the planar PQ2_0 buffer."""
+    import torch
+    out = torch.empty(kq_packed_bytes(KQ_FMT_PQ2_0, N, K), dtype=torch.uint8, device=ptq1.device)
+    kq_transcode_ptq1(ptq1, N, K, out, stream)
     return out
 
 

@@ -62,6 +62,12 @@ kq_status kq_pack_q8(const float* W, int64_t N, int64_t K, void* packed, void* s
   return launched(kq::launch_pack(kq::kFmtQ8, W, N, K, packed, as_stream(stream)));
 }
 
+kq_status kq_transcode_ptq1(const void* ptq1, int64_t N, int64_t K, void* packed, void* stream) {
+  kq_status st = check_pack(KQ_FMT_PQ2_0, ptq1, N, K, packed);
+  if (st != KQ_OK) return st;
+  return launched(kq::launch_transcode_ptq1(ptq1, N, K, packed, as_stream(stream)));
+}
+
 kq_status kq_unpack(kq_format fmt, const void* packed, int64_t N, int64_t K, float* W_out,
                     void* stream) {
   if (!fmt_ok(fmt)) return KQ_EINVAL;

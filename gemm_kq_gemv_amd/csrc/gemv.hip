@@ -279,11 +279,29 @@ __device__ __forceinline__ void pair_to_operands(const uint4& v, uint2& g0, uint
 // ones keep only about 2^-17 of it, and that must be measured against the
 // output's own sum of |w x'| (a form with a constant offset added to every
 // weight lets a large activation element with a zero weight set that scale).
+// truth table of v_bitop3_b32 for f(a, b, c): bit (a << 2 | b << 1 | c)
+template <typename F>
+constexpr uint32_t bitop3_table(F f) {
+  uint32_t t = 0;
+  for (int i = 0; i < 8; ++i) t |= (f((i >> 2) & 1, (i >> 1) & 1, i & 1) & 1u) << i;
+  return t;
+}
 __device__ __forceinline__ void ternary_fp4(uint32_t w, uint32_t& ev, uint32_t& od) {
-  const uint32_t n = ~w;
-  const uint32_t p = w & (w << 1);  // bit 2j + 1: b1 & b0 of code j
-  ev = (n & 0x11111111u) | ((n << 2) & 0x88888888u) | (p & 0x22222222u);
-  od = ((n >> 2) & 0x11111111u) | (n & 0x88888888u) | ((p >> 2) & 0x22222222u);
+  // p0..p3 are the bits of a nibble; M1 marks p0 and K marks p0, p1; forcing
+  // p2 of the last input to 1 makes its complement clear p2.  Nine
+  // instructions for 16 codes: two v_bitop3_b32 (any function of three
+  // inputs) per half, and the shifts and ors that line the bits up.
+  constexpr uint32_t M1 = 0x11111111u, K = 0x33333333u, P2 = 0x44444444u;
+  // m ? ~x : x & y  -- p0: ~b0, p1: b1 & b0
+  constexpr uint32_t kLow = bitop3_table([](int m, int x, int y) { return m ? !x : (x & y); });
+  // k ? x : ~y      -- p0, p1 from the first step; p2: 0, p3: ~b1
+  constexpr uint32_t kMix = bitop3_table([](int k, int x, int y) { return k ? x : !y; });
+  // even codes: b0 at p0, b1 at p1
+  const uint32_t xe = __builtin_amdgcn_bitop3_b32(M1, w, w << 1, kLow);
+  ev = __builtin_amdgcn_bitop3_b32(K, xe, (w << 2) | P2, kMix);
+  // odd codes: b0 at p2, b1 at p3
+  const uint32_t xo = __builtin_amdgcn_bitop3_b32(M1, w >> 2, w >> 1, kLow);
+  od = __builtin_amdgcn_bitop3_b32(K, xo, w | P2, kMix);
 }
 
 // start of part i when parts of `base` items get one more for i < rem

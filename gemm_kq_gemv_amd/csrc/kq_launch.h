@@ -41,6 +41,7 @@ inline PlanarView planar_view(int fmt, int64_t N, int64_t K, void* base) {
 // and launch_gemv_multi: -2 if no launch plan fits the arguments).
 int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed, hipStream_t st);
 int launch_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W, hipStream_t st);
+int launch_transcode_ptq1(const void* ptq1, int64_t N, int64_t K, void* packed, hipStream_t st);
 int launch_hadamard(const void* x, int x_bf16, void* xr, int xr_bf16, int64_t M, int64_t K,
                     int n, const int8_t* signs, hipStream_t st);
 

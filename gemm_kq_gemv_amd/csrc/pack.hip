@@ -1,4 +1,5 @@
-// pack.hip -- PQ2_0 / Q8_0 quantizers and dequantizers (planar layout).
+// pack.hip -- PQ2_0 / Q8_0 quantizers and dequantizers (planar layout), and
+// the PTQ1_0 -> PQ2_0 transcode.
 //
 // PQ2_0 (Bonsai 2 27B ternary g128 page, sec. 3.1): per 128-group
 // d = max|w| stored as fp16, q = round(w/d) + 1, element j in byte j/4 at bit
@@ -140,6 +141,49 @@ __global__ __launch_bounds__(256) void unpack_q8_kernel(
   reinterpret_cast<float4*>(W)[g] = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// PTQ1_0 -> PQ2_0 (Bonsai page, sec. 3.2: the two packs carry the same trits
+// and scales, so PTQ1_0 is a download format that is turned into PQ2_0 words
+// at load time).  A PTQ1_0 block is 24 bytes of five base-3 digits and 2 of
+// four, then the fp16 scale (28 bytes).  Element e of a block:
+//   e <  80: digit e / 16 of byte e % 16
+//   e < 120: digit (e - 80) / 8 of byte 16 + (e - 80) % 8
+//   else:    digit (e - 120) / 2 of byte 24 + (e - 120) % 2
+// and digit n of byte q is ((q * 3^n) mod 256) * 3 / 256 (0, 1 or 2 for any
+// byte).  Same launch shape as the packers: one thread per 32-bit PQ2_0 code
+// word (16 elements) of the padded plane; the 8 threads of a group read the
+// same 28 bytes as seven aligned words.
+__device__ __forceinline__ uint32_t ptq1_digit(uint32_t q, int n) {
+  const uint32_t p3 = n == 0 ? 1u : n == 1 ? 3u : n == 2 ? 9u : n == 3 ? 27u : 81u;
+  return (((q * p3) & 0xFFu) * 3u) >> 8;
+}
+
+__global__ __launch_bounds__(256) void transcode_ptq1_kernel(
+    const uint32_t* __restrict__ src, uint32_t* __restrict__ qs, uint16_t* __restrict__ dplane,
+    int64_t n_words, int64_t live_words, int64_t words_per_row, int64_t C) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_words) return;
+  const bool live = g < live_words;
+  const int64_t blk = g >> 3;  // block index, row-major (live words only)
+  const int i = (int)(g & 7);  // code word of the block: elements 16 i .. 16 i + 15
+  uint32_t t[7] = {0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < 7; ++k) t[k] = src[blk * 7 + k];
+  }
+  auto byte_at = [&](int k) { return (t[k >> 2] >> (8 * (k & 3))) & 0xFFu; };
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = 16 * i + j;
+    const int byte = e < 80 ? e % 16 : e < 120 ? 16 + (e - 80) % 8 : 24 + (e - 120) % 2;
+    const int n = e < 80 ? e / 16 : e < 120 ? (e - 80) / 8 : (e - 120) / 2;
+    word |= ptq1_digit(byte_at(byte), n) << (2 * j);
+  }
+  qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? word : 0u;
+  if (i == 0)
+    store_scale(dplane, g, words_per_row, C, live ? (uint16_t)(byte_at(26) | (byte_at(27) << 8)) : (uint16_t)0);
+}
+
 static int blocks_for(int64_t n) { return (int)((n + 255) / 256); }
 
 int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed,
@@ -151,6 +195,16 @@ int launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* packed,
     pack_pq2_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr, pv.d_chunks);
   else
     pack_q8_kernel<<<blocks_for(n_words), 256, 0, st>>>(W, (uint32_t*)pv.qs, (uint16_t*)pv.d, n_words, live, wpr, pv.d_chunks);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_transcode_ptq1(const void* ptq1, int64_t N, int64_t K, void* packed, hipStream_t st) {
+  PlanarView pv = planar_view(kFmtPQ2, N, K, packed);
+  const int64_t n_words = pv.qs_bytes / 4, wpr = pv.row_bytes / 4, live = N * wpr;
+  if (n_words == 0) return 0;
+  transcode_ptq1_kernel<<<blocks_for(n_words), 256, 0, st>>>((const uint32_t*)ptq1, (uint32_t*)pv.qs,
+                                                             (uint16_t*)pv.d, n_words, live, wpr,
+                                                             pv.d_chunks);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -6,6 +6,8 @@
  *        contract for a Core AI port" (Core AI model zoo knowledge page)
  *        sec. 3.1  PQ2_0 block, quantizer d = max|w|, q = round(w/d) + 1,
  *                  code q -> (q-1)*d, and the "word view" of the codes;
+ *        sec. 3.2  PTQ1_0, the same trits in base-3 bytes (load-time
+ *                  transcode to PQ2_0);
  *        sec. 4.1  R = (1/sqrt(n)) H_n S, Sylvester natural order,
  *                  applied block-diagonally along K;
  *        sec. 4.2  runtime order of a folded linear: sign flip, blockwise
@@ -116,6 +118,23 @@ kq_status kq_pack_pq2(const float *W, int64_t N, int64_t K, void *packed,
  * Errors as kq_pack_pq2, with K % 32. */
 kq_status kq_pack_q8(const float *W, int64_t N, int64_t K, void *packed,
                      void *stream);
+
+/* PTQ1_0 -> PQ2_0 at load time, [BT] 3.2: PTQ1_0 carries the same trits
+ * (code values 0, 1, 2) and fp16 scales as PQ2_0 at 1.75 bits per weight, so
+ * it is a download format that is transcoded losslessly once and then used
+ * through the PQ2_0 entry points.  ptq1: N * K/128 blocks of 28 bytes, row
+ * after row, block after block along K; each block is 24 bytes of five
+ * base-3 digits and 2 bytes of four, then the fp16 scale (little endian,
+ * last).  Element e of a block is digit e/16 of byte e%16 (e < 80), digit
+ * (e-80)/8 of byte 16 + (e-80)%8 (e < 120), or digit (e-120)/2 of byte
+ * 24 + (e-120)%2; digit n of byte q is ((q * 3^n) mod 256) * 3 / 256, the
+ * first digit most significant.  Every byte value decodes.  Writes the planar
+ * PQ2_0 buffer `packed` (kq_packed_bytes(KQ_FMT_PQ2_0, N, K) bytes) exactly as
+ * kq_pack_pq2 would lay out the same codes and scales.
+ * Errors: KQ_EINVAL (NULL, negative size), KQ_ESHAPE (N < 1, K < 128,
+ * K % 128), KQ_EALIGN. */
+kq_status kq_transcode_ptq1(const void *ptq1, int64_t N, int64_t K,
+                            void *packed, void *stream);
 
 /* Dequantize a planar buffer to fp32 W_out [N][K]: (q-1)*d for PQ2_0 (a
  * foreign code 3 decodes to 2*d), d*q for Q8_0 ([BT] 3.1, [KB]).  Exact.

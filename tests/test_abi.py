@@ -106,6 +106,10 @@ def test_pack_rejections():
     assert _status(kq.kq_pack_pq2, MISALIGNED, 4, 128, FAKE, 0) == "KQ_EALIGN"
     assert _status(kq.kq_pack_q8, FAKE, 4, 48, FAKE, 0) == "KQ_ESHAPE"
     assert _status(kq.kq_pack_q8, FAKE, 4, 32, MISALIGNED, 0) == "KQ_EALIGN"
+    assert _status(kq.kq_transcode_ptq1, None, 4, 128, FAKE, 0) == "KQ_EINVAL"
+    assert _status(kq.kq_transcode_ptq1, FAKE, 4, 96, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(kq.kq_transcode_ptq1, FAKE, 0, 128, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(kq.kq_transcode_ptq1, FAKE, 4, 128, MISALIGNED, 0) == "KQ_EALIGN"
     assert _status(kq.kq_unpack, 7, FAKE, 4, 128, FAKE, 0) == "KQ_EINVAL"
     assert _status(kq.kq_unpack, 1, FAKE, 4, 160, FAKE, 0) == "KQ_ESHAPE"
 

@@ -132,3 +132,53 @@ def test_pack_unpack_roundtrip_c2_shape():
     # and repacking the dequantized weights reproduces the bytes
     again = kq.pack(1, dev(Wd))
     assert np.array_equal(host(again), host(packed))
+
+
+# ---- PTQ1_0 -> PQ2_0 load-time transcode (Bonsai page, sec. 3.2) ----------
+
+@pytest.mark.parametrize("N,K", [(1, 128), (17, 640), (37, 5120), (100, 17408)])
+def test_transcode_ptq1_bit_exact(N, K):
+    """PTQ1_0 blocks made by the oracle from quantized weights: the GPU's
+    planar PQ2_0 bytes equal the oracle's transcode laid out planar, and equal
+    what kq_pack_pq2 writes for the same weights."""
+    import torch
+    kq = _kq()
+    W = special_weights(2100 + N, N, K, 128)
+    aos = oracle.pack_pq2_aos(W)
+    p1 = oracle.pq2_to_ptq1_aos(aos, N, K)
+    want = oracle.aos_to_planar(1, oracle.ptq1_to_pq2_aos(p1, N, K), N, K)
+    nb = kq.kq_packed_bytes(1, N, K)
+    buf = torch.full((nb + 1024,), 0xA5, dtype=torch.uint8, device="cuda")
+    kq.kq_transcode_ptq1(dev(p1), N, K, buf)
+    got = host(buf)
+    assert np.array_equal(got[:nb], want)
+    assert np.all(got[nb:] == 0xA5), "write past the end of the packed buffer"
+    assert np.array_equal(got[:nb], host(kq.pack(1, dev(W))))
+
+
+@pytest.mark.parametrize("N,K", [(3, 256), (33, 1152)])
+def test_transcode_ptq1_every_byte_value(N, K):
+    """Arbitrary blobs (every byte value at every trit position) decode as the
+    oracle decodes them."""
+    kq = _kq()
+    p1 = inputs.random_bytes(2200 + N, N * (K // 128) * 28)
+    want = oracle.aos_to_planar(1, oracle.ptq1_to_pq2_aos(p1, N, K), N, K)
+    got = host(kq.transcode_ptq1(dev(p1), N, K))
+    assert np.array_equal(got, want)
+    # the decoded values are the oracle's PTQ1_0 reading (random scale bytes
+    # include NaN and infinite halves: NaN compares equal to NaN here)
+    deq = host(kq.unpack(1, kq.transcode_ptq1(dev(p1), N, K), N, K))
+    assert np.array_equal(deq.astype(np.float64), oracle.unpack_ptq1_aos(p1, N, K), equal_nan=True)
+
+
+def test_transcode_ptq1_gemv_matches_pq2():
+    """A GEMV over transcoded PTQ1_0 weights is bitwise the GEMV over the same
+    weights packed as PQ2_0 (the buffers are identical)."""
+    kq = _kq()
+    N, K = 10240, 5120
+    W = inputs.weights(1002, N, K)
+    p1 = oracle.pq2_to_ptq1_aos(oracle.pack_pq2_aos(W), N, K)
+    x = dev(inputs.activations(2002, 1, K))
+    a = host(kq.gemv(1, kq.transcode_ptq1(dev(p1), N, K), N, K, x, 128))
+    b = host(kq.gemv(1, kq.pack(1, dev(W)), N, K, x, 128))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
