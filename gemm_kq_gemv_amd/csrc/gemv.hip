@@ -1433,6 +1433,17 @@ __global__ __launch_bounds__(1024) void gemv_loads_twin_kernel(GemvArgs a, int M
   WBuf<GS> wb[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) issue(i, wb[i]);
+  if (PQ2 && nrb <= D) {
+    // as the PQ2_0 GEMV: every row block is in flight, no further loads
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i < nrb) {
+#pragma unroll
+        for (int q = 0; q < GS / 2; ++q) acc ^= wb[i].q[q].x ^ wb[i].q[q].y ^ wb[i].q[q].z ^ wb[i].q[q].w ^ wb[i].d[q];
+      }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+    return;
+  }
   for (int j0 = 0; j0 < nrb; j0 += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
