@@ -247,13 +247,13 @@ def gemv_multi(fmt: int, packed, N, K: int, x, block_len: int, signs=None, y=Non
     return y
 
 
-def gemm(packed, N: int, K: int, x, block_len: int, signs=None, ws=None, y=None, stream=None):
+def gemm(packed, N: int, K: int, x, block_len: int, signs=None, ws=None, y=None, stream=None,
+         fmt: int = KQ_FMT_PQ2_0):
     import torch
     M = x.shape[0]
     if ws is None:
-        ws, _ = workspace(1, KQ_FMT_PQ2_0, M, N, K, block_len, 0, device=x.device)
+        ws, _ = workspace(1, fmt, M, N, K, block_len, 0, device=x.device)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    kq_gemm(KQ_FMT_PQ2_0, packed, N, K, x, _dtype_code(x), M, block_len, signs, y, ws,
-            ws.numel(), stream)
+    kq_gemm(fmt, packed, N, K, x, _dtype_code(x), M, block_len, signs, y, ws, ws.numel(), stream)
     return y

@@ -148,7 +148,6 @@ kq_status kq_gemm(kq_format fmt, const void* packed, int64_t N, int64_t K, const
                   kq_dtype x_dt, int64_t M, int32_t block_len, const int8_t* signs, float* y,
                   void* workspace, size_t ws_bytes, void* stream) {
   if (!fmt_ok(fmt) || !dtype_ok(x_dt) || !packed || !x || !y) return KQ_EINVAL;
-  if (fmt != KQ_FMT_PQ2_0) return KQ_EUNSUPPORTED;
   if (N < 0 || K < 0 || M < 0) return KQ_EINVAL;
   if (!shape_ok(fmt, N, K) || M < 1 || M > (int64_t(1) << 40) / K || !block_len_ok(block_len) ||
       (block_len > 0 && K % block_len))
@@ -160,7 +159,7 @@ kq_status kq_gemm(kq_format fmt, const void* packed, int64_t N, int64_t K, const
   const int64_t need = kq::gemm_workspace_bytes(M, N, K, block_len, x_dt == KQ_BF16, signs);
   const bool uses_ws = block_len > 0 || signs || x_dt != KQ_BF16;
   if (uses_ws && (!workspace || (int64_t)ws_bytes < need)) return KQ_EWORKSPACE;
-  return launched(kq::launch_gemm(packed, N, K, x, x_dt == KQ_BF16, M, block_len, signs, y,
+  return launched(kq::launch_gemm(fmt, packed, N, K, x, x_dt == KQ_BF16, M, block_len, signs, y,
                                   workspace, as_stream(stream)));
 }
 

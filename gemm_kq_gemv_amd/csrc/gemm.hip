@@ -1,37 +1,46 @@
-// gemm.hip -- PQ2_0 prefill GEMM on bf16 MFMA.
+// gemm.hip -- prefill GEMM on bf16 MFMA for PQ2_0 and Q8_0 weights.
 //
-// y[m][n] = sum_k bf16((q-1)*d)[n][k] * bf16(x'[m][k]), fp32 accumulation.
-// Each weight block is dequantized once per LDS tile and the tile is reused
-// by every token row of the workgroup (the dequantize-once-per-tile prefill
-// scheme of the Kipp Benchmarks page, "Quantized projections on the tensor
-// units"; the Bonsai page's tiled ternary GEMM, sec. 8.3, 8.5).
+// y[m][n] = sum_k bf16(deq(W)[n][k]) * bf16(x'[m][k]), fp32 accumulation, with
+// deq = (q-1)*d for PQ2_0 (Bonsai ternary g128 page, sec. 3.1) and d*q for
+// Q8_0 (Kipp pages, "Weight quantization").  Each weight block is dequantized
+// once per LDS tile and the tile is reused by every token row of the
+// workgroup (the dequantize-once-per-tile prefill scheme of the Kipp
+// Benchmarks page, "Quantized projections on the tensor units"; the Bonsai
+// page's tiled ternary GEMM and its chunked prefill, sec. 8.3).
 //
 // gfx950 design
 // -------------
-// * Block tile 256 (tokens) x 160 (weight rows) x 64 (K), 4 waves in a 2 x 2
-//   arrangement; each wave owns 128 x 80 outputs = 8 x 5 accumulators of
-//   v_mfma_f32_16x16x32_bf16 (160 fp32 registers).  At M = 2048, N = 10240
-//   that is 512 tiles, two per CU, with no tail imbalance.
+// * Block tiles TM (tokens) x TN (weight rows) x 64 (K), 4 waves in a
+//   WGM x WGN arrangement, each wave owning (TM / WGM) x (TN / WGN) outputs as
+//   v_mfma_f32_16x16x32_bf16 accumulators.  Three instances:
+//     256 x 160, waves 2 x 2 (128 x 80 each, 40 accumulators): prompts; at
+//       M = 2048, N = 10240 that is 512 tiles, two per CU, with no tail;
+//     64 x 64 and 16 x 64, waves 1 x 4 (one 16-column slice each): the
+//       64- and 16-token chunks of a chunked prefill, where a 256-token tile
+//       would spend 3/4 or 15/16 of its matrix-core work on padding rows.
 // * Two LDS stages of x' (bf16) and the dequantized weight tile, 128-byte
 //   rows with the 16-byte chunks XOR-swizzled by (row / 2) % 8, so that the
 //   16-byte operand reads of 16 rows and the row-contiguous writes are both
-//   bank-conflict free without padding (2 x 52 KiB).  With the 72-element
-//   padded rows used before, a quarter of the LDS cycles were bank
-//   conflicts (SQ_LDS_BANK_CONFLICT).
+//   bank-conflict free without padding.  With 72-element padded rows, a
+//   quarter of the LDS cycles were bank conflicts (SQ_LDS_BANK_CONFLICT).
 // * Software pipeline, one barrier per K-tile.  The MFMAs always run from
-//   registers: while the 40 MFMAs of k-step 0 of tile t run, the operands of
-//   its k-step 1 are read, tile t + 1 is dequantized and written to the
-//   other stage and tile t + 2 is fetched into the staging registers; after
-//   the barrier, the 40 MFMAs of k-step 1 overlap the reads of tile t + 1's
-//   k-step 0.  The stage written in the first half was last read before the
-//   previous barrier.
-// * Dequantization: the 160 x 64 codes of a tile are 1280 units of 8 codes,
-//   five per thread: fp4 conversion of the nibble-spread codes gives c
-//   exactly, c*d - d is exact in fp32, and v_cvt_pk_bf16_f32 rounds pairs to
-//   bf16 (nearest even) -- the same value as (q-1) * bf16(d).
+//   registers: while the MFMAs of k-step 0 of tile t run, the operands of its
+//   k-step 1 are read, tile t + 1 is dequantized and written to the other
+//   stage and tile t + 2 is fetched into the staging registers; after the
+//   barrier, the MFMAs of k-step 1 overlap the reads of tile t + 1's k-step 0.
+//   The stage written in the first half was last read before the previous
+//   barrier.
+// * Dequantization, eight weights per unit (a 64-wide K-tile row is 8 units):
+//   PQ2_0: fp4 conversion of nibble-spread codes gives c exactly, c*d - d is
+//   exact in fp32; Q8_0: each int8 converts exactly and q*d is exact in fp32.
+//   v_cvt_pk_bf16_f32 rounds pairs to bf16 (nearest even).
+// * All global loads go through buffer resources that cover exactly the
+//   tile's valid rows, with the whole offset in the range-checked vector
+//   offset, so rows past M or N (and K-tiles past the end) read zeros with no
+//   branch.
 // * Tile order is XCD-aware: the 8 XCDs each take a contiguous eighth of the
 //   token tiles and walk every weight tile over it, so the x' rows stay in
-//   that XCD's L2 while the (ten times smaller) weight tiles stream past.
+//   that XCD's L2 while the weight tiles stream past.
 #include <type_traits>
 
 #include "kq_device.h"
@@ -41,17 +50,26 @@ namespace kq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int TM = 256, TN = 160, TK = 64;
-constexpr int ROWB = TK * 2;                        // bytes per LDS row (no padding)
-constexpr int A_BYTES = TM * ROWB;                  // 32 KiB
-constexpr int B_BYTES = TN * ROWB;                  // 20 KiB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;      // 52 KiB
-constexpr int NSTAGE = 2;
-constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
-constexpr int WM = TM / 2, WN = TN / 2;             // wave tile 128 x 80
-constexpr int FM = WM / 16, FN = WN / 16;           // 8 x 5 MFMA tiles per wave
-constexpr int UNITS = TN * TK / 8 / 256;            // 8-code units per thread per tile (5)
-static_assert(TN * TK / 8 == UNITS * 256, "units must divide evenly");
+constexpr int TK = 64;
+constexpr int ROWB = TK * 2;  // bytes per LDS row (no padding)
+
+template <int FMT, int TM_, int TN_, int WGM_, int WGN_>
+struct GemmCfg {
+  static constexpr int TM = TM_, TN = TN_, WGM = WGM_, WGN = WGN_;
+  static_assert(WGM * WGN == 4, "four waves");
+  static constexpr int WM = TM / WGM, WN = TN / WGN;   // wave tile
+  static constexpr int FM = WM / 16, FN = WN / 16;     // MFMA tiles per wave
+  static_assert(FM >= 1 && FN >= 1 && FM * 16 == WM && FN * 16 == WN, "whole MFMA tiles");
+  static_assert(FM >= FN, "B operands are refilled inside the A loop");
+  static constexpr int AROWS = TM < 32 ? 32 : TM;      // LDS rows of the x' tile
+  static constexpr int ALOADS = AROWS / 32;            // 16-byte x' chunks per thread
+  static constexpr int UNITS = TN * TK / 8 / 256;      // 8-weight units per thread
+  static_assert(TN * TK / 8 == UNITS * 256, "units must divide evenly");
+  static constexpr int A_BYTES = AROWS * ROWB;
+  static constexpr int B_BYTES = TN * ROWB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+};
 
 struct GemmArgs {
   const uint16_t* xb;   // x' bf16 [M][K]
@@ -59,14 +77,14 @@ struct GemmArgs {
   const uint8_t* dpl;   // scale plane (16-row x 8-block chunks)
   float* y;             // [M][N]
   int64_t M, N, K;
-  int64_t d_per_row;    // blocks per row (K / 128)
+  int64_t d_per_row;    // blocks per row (K / 128 or K / 32)
   int64_t d_tile_bytes; // scale bytes per 16-row tile
   int mt, nt;           // tile counts
 };
 
-// 8 codes (16 bits, code j at bits 2j) -> 8 bf16 values (q-1)*d, as 4 dwords
-// in element order
-__device__ __forceinline__ uint4 dequant8_bf16(uint32_t h, float d) {
+// 8 PQ2_0 codes (16 bits, code j at bits 2j) -> 8 bf16 values (q-1)*d, as 4
+// dwords in element order
+__device__ __forceinline__ uint4 dequant8_pq2(uint32_t h, float d) {
   const uint32_t e = h & 0x3333u;         // codes 0, 2, 4, 6 in nibbles 0..3
   const uint32_t o = (h >> 2) & 0x3333u;  // codes 1, 3, 5, 7
   const f32x2 e0 = codes2<0>(e), e1 = codes2<1>(e), o0 = codes2<0>(o), o1 = codes2<1>(o);
@@ -75,34 +93,54 @@ __device__ __forceinline__ uint4 dequant8_bf16(uint32_t h, float d) {
                     pack_bf16x2(fmaf(e1.x, d, -d), fmaf(o1.x, d, -d)),
                     pack_bf16x2(fmaf(e1.y, d, -d), fmaf(o1.y, d, -d)));
 }
+// 8 Q8_0 codes (int8, element j in byte j of the pair) -> 8 bf16 values q*d
+__device__ __forceinline__ uint4 dequant8_q8(uint2 w, float d) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = (float)(int8_t)(w.x >> (8 * j)) * d;
+    v[4 + j] = (float)(int8_t)(w.y >> (8 * j)) * d;
+  }
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
 
-// buffer loads with a per-thread offset and a uniform (scalar) one
-__device__ __forceinline__ uint4 load16_s(BufRsrc r, uint32_t voff, uint32_t soff) {
+// buffer loads with the whole offset per lane (range-checked)
+__device__ __forceinline__ uint4 load16(BufRsrc r, uint32_t off) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ uint32_t load4_s(BufRsrc r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+__device__ __forceinline__ uint2 load8(BufRsrc r, uint32_t off) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v.x, v.y);
 }
-__device__ __forceinline__ uint32_t load2_s(BufRsrc r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+__device__ __forceinline__ uint32_t load4(BufRsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t load2(BufRsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
+template <typename Cfg, int FMT>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
+  constexpr int ALOADS = Cfg::ALOADS, UNITS = Cfg::UNITS;
+  constexpr int A_BYTES = Cfg::A_BYTES, STAGE_BYTES = Cfg::STAGE_BYTES;
+  constexpr bool PQ2 = FMT == kFmtPQ2;
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 
   // ---- XCD-aware tile mapping
   const int bid = blockIdx.x;
   int m_tile, n_tile;
   if ((a.mt & 7) == 0) {
     // XCD x takes an eighth of the token tiles and walks every weight tile
-    // over them: its x' rows (2.6 MB per token tile at K = 5120) stay in its
-    // L2 while the weight tiles, a tenth of the size, stream past
+    // over them: its x' rows stay in its L2 while the weight tiles stream past
     const int xcd = bid & 7, local = bid >> 3;
     m_tile = xcd * (a.mt >> 3) + local / a.nt;
     n_tile = local % a.nt;
@@ -117,20 +155,14 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   }
   const int64_t m0 = (int64_t)m_tile * TM, n0 = (int64_t)n_tile * TN;
 
-  // ---- global load geometry.  K order inside a tile: the two K-tiles of a
-  // 128-element block interleave in runs of 8, so chunk c (8 elements) of
-  // K-tile 2b + h holds elements 16 c + 8 h .. +7 of block b.  The product
-  // is a sum over K, so any order shared by both operands gives it; this one
-  // puts a thread's codes for both K-tiles of a block in one 4-byte word.
-  // x' tile: load i of thread t covers row 32 i + t / 8, chunk t % 8.
-  // Weights: unit i of thread t is weight row 32 i + t / 8, chunk t % 8: 16
-  // bits of a 4-byte word loaded once per block (the low half for the even
-  // K-tile), with the block's scale.
-  // All go through buffer resources that cover exactly the block's valid
-  // rows (the code and scale resources: its valid 16-row tiles, whose rows
-  // past N hold zero codes and zero scales), with the whole offset in the
-  // range-checked vector offset, so rows past M or N read zeros with no
-  // branch: code 0 with scale 0 dequantizes to 0.
+  // ---- global load geometry.  Thread t stages x' chunk t % 8 (8 bf16) of
+  // rows t / 8 + 32 i, and weight units (rows t / 8 + 32 i, chunk t % 8).
+  // K order inside a tile: PQ2_0 interleaves the two K-tiles of a 128-block in
+  // runs of 8 (chunk c of K-tile 2b + h holds elements 16 c + 8 h .. + 7 of
+  // block b), so that one 4-byte word per unit brings a thread's codes for
+  // both K-tiles; Q8_0 keeps the natural order (chunk c of K-tile t holds
+  // elements 64 t + 8 c .. + 7, bytes 8 (c % 4) .. + 7 of block 2 t + c / 4).
+  // The product is a sum over K, so any order shared by both operands gives it.
   const int arow = tid >> 3, achunk = tid & 7;
   const int64_t G = a.d_per_row;
   const int64_t arows = a.M - m0 < TM ? a.M - m0 : TM;
@@ -138,54 +170,76 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   const BufRsrc ra_rs = make_rsrc(a.xb + m0 * a.K, (uint32_t)(arows * a.K * 2));
   const BufRsrc rq_rs = make_rsrc(a.qs + (n0 >> 4) * G * 512, (uint32_t)((brows + 15) / 16 * G * 512));
   const BufRsrc rd_rs = make_rsrc(a.dpl + (n0 >> 4) * a.d_tile_bytes, (uint32_t)((brows + 15) / 16 * a.d_tile_bytes));
-  const uint32_t a_off = (uint32_t)(arow * a.K + achunk * 16) * 2u;
-  // unit i: row 32 i + t / 8 = 16-row tile (t / 128 + 2 i), row (t / 8) % 16
-  const uint32_t q_off = (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + achunk * 4);
+  const uint32_t a_off = (uint32_t)(arow * a.K + achunk * (PQ2 ? 16 : 8)) * 2u;
+  const uint32_t rowstep = (uint32_t)(32 * a.K * 2);
+  // unit i: weight row 32 i + t / 8 = 16-row tile (t / 128 + 2 i), row (t / 8) % 16
+  const uint32_t q_off = PQ2 ? (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + achunk * 4)
+                             : (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + (achunk & 3) * 8 +
+                                          (achunk >> 2) * 512);
   const uint32_t q_step = (uint32_t)(2 * G * 512);  // two 16-row tiles
   const uint32_t d_off = (uint32_t)((tid >> 7) * a.d_tile_bytes + ((tid >> 3) & 15) * 16);
   const uint32_t d_step = (uint32_t)(2 * a.d_tile_bytes);
+  // K-tiles: PQ2_0 has an even number (K is a multiple of 128); Q8_0 may end
+  // in half a tile (K a multiple of 32), whose chunks past K load nothing
+  const int KT = (int)((a.K + TK - 1) / TK);
 
-  // LDS byte offset of this thread's 16-byte chunk in rows arow + 32 i (A)
-  // and in weight rows arow + 32 i (B): row * 128 + (chunk ^ (row / 2) % 8) * 16,
-  // and (row / 2) % 8 = (t / 16) % 8 for every i
+  // LDS byte offset of this thread's 16-byte chunk in rows arow + 32 i:
+  // row * 128 + (chunk ^ (row / 2) % 8) * 16, and (row / 2) % 8 = (t / 16) % 8
   const uint32_t w_lds = (uint32_t)(arow * ROWB + ((achunk ^ ((tid >> 4) & 7)) << 4));
 
   // staging registers: the tile written to LDS at the start of iteration t
-  // was fetched at the start of iteration t - 1; the weight words and scales
-  // of a block are fetched with its even K-tile and serve both
-  const int KT = (int)(a.K / TK);  // even: K is a multiple of 128
-  uint4 ra[8];
-  uint32_t rq[UNITS];
+  // was fetched at the start of iteration t - 1 (PQ2_0: a block's words and
+  // scales are fetched with its even K-tile and serve both)
+  uint4 ra[ALOADS];
+  uint32_t rq[PQ2 ? UNITS : 1];
+  uint2 rq8[PQ2 ? 1 : UNITS];
   uint32_t rdd[UNITS];
-  // Every offset goes into the per-lane (vector) offset: the hardware range
-  // check of a raw buffer load covers the vector offset only, not the scalar
-  // one.  K-tiles past the end (the prefetches of the last two iterations)
-  // load at kOutOfRange.
-  auto gload = [&](int kt, bool with_b) {
-    const bool in_k = kt < KT;
-    const uint32_t kb = (uint32_t)kt >> 1, h = (uint32_t)kt & 1u;
-    const uint32_t rowstep = (uint32_t)(32 * a.K * 2);
-    const uint32_t ak = a_off + (kb * 128 + h * 8) * 2;
+  auto gload = [&](int kt) {
+    // the prefetches of the last two iterations load nothing
+    const bool in_k = PQ2 ? kt < KT : (int64_t)kt * TK + 8 * achunk < a.K;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = load16_s(ra_rs, in_k ? ak + i * rowstep : kOutOfRange, 0);
-    if (with_b) {
-      const uint32_t qk = q_off + kb * 512;
-      const uint32_t dk = d_off + (kb >> 3) * 256 + (kb & 7) * 2;
+    for (int i = 0; i < ALOADS; ++i) {
+      const uint32_t ak = PQ2 ? a_off + (uint32_t)(((kt >> 1) * 128 + (kt & 1) * 8) * 2)
+                              : a_off + (uint32_t)(kt * TK * 2);
+      // rows past TM (the 16-token tile stages 32 LDS rows) load nothing
+      const bool in_m = 32 * i + arow < TM;
+      ra[i] = load16(ra_rs, in_k && in_m ? ak + i * rowstep : kOutOfRange);
+    }
+    if constexpr (PQ2) {
+      if ((kt & 1) == 0) {
+        const uint32_t kb = (uint32_t)kt >> 1;
+        const uint32_t qk = q_off + kb * 512;
+        const uint32_t dk = d_off + (kb >> 3) * 256 + (kb & 7) * 2;
+#pragma unroll
+        for (int i = 0; i < UNITS; ++i) {
+          rq[i] = load4(rq_rs, in_k ? qk + i * q_step : kOutOfRange);
+          rdd[i] = load2(rd_rs, in_k ? dk + i * d_step : kOutOfRange);
+        }
+      }
+    } else {
+      // the unit's 32-block: 2 kt + chunk / 4
+      const uint32_t b = 2u * (uint32_t)kt + ((uint32_t)achunk >> 2);
+      const uint32_t qk = q_off + (uint32_t)kt * 1024u;
+      const uint32_t dk = d_off + (b >> 3) * 256 + (b & 7) * 2;
 #pragma unroll
       for (int i = 0; i < UNITS; ++i) {
-        rq[i] = load4_s(rq_rs, in_k ? qk + i * q_step : kOutOfRange, 0);
-        rdd[i] = load2_s(rd_rs, in_k ? dk + i * d_step : kOutOfRange, 0);
+        rq8[i] = load8(rq_rs, in_k ? qk + i * q_step : kOutOfRange);
+        rdd[i] = load2(rd_rs, in_k ? dk + i * d_step : kOutOfRange);
       }
     }
   };
-  auto sstore = [&](int stage, int h) {
+  auto sstore = [&](int stage, int kt) {
     uint8_t* S = smem + stage * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(S + w_lds + i * 32 * ROWB) = ra[i];
+    for (int i = 0; i < ALOADS; ++i) *reinterpret_cast<uint4*>(S + w_lds + i * 32 * ROWB) = ra[i];
 #pragma unroll
-    for (int i = 0; i < UNITS; ++i)
-      *reinterpret_cast<uint4*>(S + A_BYTES + w_lds + i * 32 * ROWB) =
-          dequant8_bf16(rq[i] >> (16 * h), f16_bits_to_f32(rdd[i]));
+    for (int i = 0; i < UNITS; ++i) {
+      const float d = f16_bits_to_f32(rdd[i]);
+      uint4 v;
+      if constexpr (PQ2) v = dequant8_pq2(rq[i] >> (16 * (kt & 1)), d);
+      else v = dequant8_q8(rq8[i], d);
+      *reinterpret_cast<uint4*>(S + A_BYTES + w_lds + i * 32 * ROWB) = v;
+    }
   };
 
   f32x4 acc[FM][FN];
@@ -204,7 +258,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   const uint32_t b_rd0 = (uint32_t)(A_BYTES + (wn * WN + fr) * ROWB) + sw;
   const uint32_t a_rd1 = a_rd0 ^ 64u, b_rd1 = b_rd0 ^ 64u;
   // one set of A operands, refilled row tile by row tile as the MFMAs release
-  // them; two sets of B operands (all five are used by every row tile)
+  // them; two sets of B operands (all are used by every row tile)
   bf16x8 fa[FM], fb[2][FN];
   auto lda = [&](int stage, int ks, int i) {
     return *reinterpret_cast<const bf16x8*>(smem + stage * STAGE_BYTES + (ks ? a_rd1 : a_rd0) + i * 16 * ROWB);
@@ -212,8 +266,8 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   auto ldb = [&](int stage, int ks, int j) {
     return *reinterpret_cast<const bf16x8*>(smem + stage * STAGE_BYTES + (ks ? b_rd1 : b_rd0) + j * 16 * ROWB);
   };
-  // the 40 MFMAs of one k-step with B set `cur`, reading the operands of the
-  // next k-step (stage `ns`, k-step `nks`) into A and B set `cur ^ 1`
+  // the MFMAs of one k-step with B set `cur`, reading the operands of the next
+  // k-step (stage `ns`, k-step `nks`) into A and B set `cur ^ 1`
   auto mma = [&](int cur, int ns, int nks) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -224,12 +278,39 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
       if (i < FN) fb[cur ^ 1][i] = ldb(ns, nks, i);
     }
   };
+  // scheduling hints for the 256 x 160 tile: spread the staging (loads,
+  // dequantization, LDS writes) between its MFMAs
+  auto hints0 = [&]() {
+    if constexpr (FM == 8 && FN == 5) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (j == 1 || j == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+        if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+  auto hints1 = [&]() {
+    if constexpr (FM == 8 && FN == 5) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
 
   // prologue: tiles 0 and 1 to stages 0 and 1, tiles 2 and 3 in flight,
   // the first k-step's operands in registers
-  gload(0, true);
+  gload(0);
   sstore(0, 0);
-  gload(1, false);
+  gload(1);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa[i] = lda(0, 0, i);
@@ -237,48 +318,37 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   for (int j = 0; j < FN; ++j) fb[0][j] = ldb(0, 0, j);
 
   // iteration t: stage t % 2 holds tile t.  First half: k-step 0 of tile t
-  // from registers while its k-step 1 is read, tile t + 1 (fetched during
-  // the last iteration) is written to the other stage and tile t + 2 is
-  // fetched.  Second half, after the barrier: k-step 1 while the next tile's
-  // k-step 0 is read.  The other stage was last read before the previous
-  // barrier, so one barrier per tile suffices.
+  // from registers while its k-step 1 is read, tile t + 1 (fetched during the
+  // last iteration) is written to the other stage and tile t + 2 is fetched.
+  // Second half, after the barrier: k-step 1 while the next tile's k-step 0 is
+  // read.  The other stage was last read before the previous barrier, so one
+  // barrier per tile suffices.
   auto iter = [&](int t, auto STAGE) {
     constexpr int st = decltype(STAGE)::value;
     __builtin_amdgcn_sched_barrier(0);
-    sstore(st ^ 1, st ^ 1);
-    gload(t + 2, st == 0);
+    sstore(st ^ 1, t + 1);
+    gload(t + 2);
     mma(0, st, 1);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (j == 1 || j == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      }
-      if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    hints0();
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     mma(1, st ^ 1, 0);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    hints1();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // the last two tiles are peeled off the loop: with them inside, the
-  // compiler moved the accumulators between register files every iteration
+  // the last tiles are peeled off the loop: with them inside, the compiler
+  // moved the accumulators between register files every iteration
   int t = 0;
   for (; t + 2 < KT; t += 2) {
     iter(t, std::integral_constant<int, 0>{});
     iter(t + 1, std::integral_constant<int, 1>{});
   }
-  iter(t, std::integral_constant<int, 0>{});
-  iter(t + 1, std::integral_constant<int, 1>{});
+  if (t + 1 < KT) {
+    iter(t, std::integral_constant<int, 0>{});
+    iter(t + 1, std::integral_constant<int, 1>{});
+  } else {
+    iter(t, std::integral_constant<int, 0>{});  // Q8_0 with an odd number of K-tiles
+  }
 
   // ---- epilogue: lane (j, q), register r -> row 4q + r, column j of a tile
 #pragma unroll
@@ -295,12 +365,22 @@ __global__ __launch_bounds__(256, 1) void gemm_pq2_kernel(GemmArgs a) {
   }
 }
 
+// Token-tile instances: the 256 x 160 prompt tile, and 64- / 16-token tiles
+// of 64 weight rows for short chunks.
+template <int FMT> using CfgBig = GemmCfg<FMT, 256, 160, 2, 2>;
+template <int FMT> using Cfg64 = GemmCfg<FMT, 64, 64, 1, 4>;
+template <int FMT> using Cfg16 = GemmCfg<FMT, 16, 64, 1, 4>;
+
+// token tile for M tokens: 16 up to 16, 64 up to 96, else 256
+static int gemm_tile_m(int64_t M) { return M <= 16 ? 16 : (M <= 96 ? 64 : 256); }
+
 // 32-bit buffer ranges and offsets: a 256-row x' tile spans 512 K bytes,
 // which must stay below the out-of-range offset (kOutOfRange, about 2^31);
 // the tile grid must fit an int.
 bool gemm_shape_supported(int64_t M, int64_t N, int64_t K) {
   if (K > kGemmMaxK) return false;
-  const int64_t mt = (M + TM - 1) / TM, nt = (N + TN - 1) / TN;
+  const int tm = gemm_tile_m(M), tn = tm == 256 ? 160 : 64;
+  const int64_t mt = (M + tm - 1) / tm, nt = (N + tn - 1) / tn;
   return mt * nt <= 0x7FFFFFFF;
 }
 
@@ -310,14 +390,39 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int
   return (M * K * 2 + 255) / 256 * 256;
 }
 
-int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_bf16, int64_t M,
-                int block_len, const int8_t* signs, float* y, void* ws, hipStream_t st) {
+template <typename Cfg, int FMT>
+static int launch_tile(const GemmArgs& base, hipStream_t st) {
+  GemmArgs a = base;
+  a.mt = (int)((a.M + Cfg::TM - 1) / Cfg::TM);
+  a.nt = (int)((a.N + Cfg::TN - 1) / Cfg::TN);
+  // more than 64 KiB of dynamic LDS needs the attribute; set once per
+  // instance (thread-safe static initialisation)
+  static const bool attr_ok =
+      Cfg::LDS_BYTES <= 64 * 1024 ||
+      hipFuncSetAttribute((const void*)gemm_kernel<Cfg, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          Cfg::LDS_BYTES) == hipSuccess;
+  if (!attr_ok) return -1;
+  gemm_kernel<Cfg, FMT><<<a.mt * a.nt, 256, Cfg::LDS_BYTES, st>>>(a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int FMT>
+static int launch_fmt(const GemmArgs& a, hipStream_t st) {
+  switch (gemm_tile_m(a.M)) {
+    case 16: return launch_tile<Cfg16<FMT>, FMT>(a, st);
+    case 64: return launch_tile<Cfg64<FMT>, FMT>(a, st);
+    default: return launch_tile<CfgBig<FMT>, FMT>(a, st);
+  }
+}
+
+int launch_gemm(int fmt, const void* packed, int64_t N, int64_t K, const void* x, int x_bf16,
+                int64_t M, int block_len, const int8_t* signs, float* y, void* ws, hipStream_t st) {
   const uint16_t* xb = (const uint16_t*)x;
   if (block_len > 0 || signs || !x_bf16) {
     if (launch_hadamard(x, x_bf16, ws, 1, M, K, block_len > 0 ? block_len : 1, signs, st)) return -1;
     xb = (const uint16_t*)ws;
   }
-  PlanarView pv = planar_view(kFmtPQ2, N, K, const_cast<void*>(packed));
+  PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
   GemmArgs a;
   a.xb = xb;
   a.qs = pv.qs;
@@ -328,16 +433,8 @@ int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_b
   a.K = K;
   a.d_per_row = pv.d_per_row;
   a.d_tile_bytes = pv.d_tile_bytes;
-  a.mt = (int)((M + TM - 1) / TM);
-  a.nt = (int)((N + TN - 1) / TN);
-  // the kernel needs more than 64 KiB of dynamic LDS; set once (thread-safe
-  // static initialisation)
-  static const bool attr_ok =
-      hipFuncSetAttribute((const void*)gemm_pq2_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          GEMM_LDS_BYTES) == hipSuccess;
-  if (!attr_ok) return -1;
-  gemm_pq2_kernel<<<a.mt * a.nt, 256, GEMM_LDS_BYTES, st>>>(a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  a.mt = a.nt = 0;
+  return fmt == kFmtPQ2 ? launch_fmt<kFmtPQ2>(a, st) : launch_fmt<kFmtQ8>(a, st);
 }
 
 }  // namespace kq

@@ -74,6 +74,7 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
 
 // Largest K the prefill GEMM takes: a 256-row activation tile (256 * K * 2
 // bytes) stays a 32-bit buffer range well below the out-of-range offset.
+// gemm_shape_supported also bounds the tile count by an int.
 constexpr int64_t kGemmMaxK = int64_t(1) << 21;
 bool gemm_shape_supported(int64_t M, int64_t N, int64_t K);
 // Loads-only twin of launch_gemv (same plan and weight loads, no arithmetic);
@@ -87,7 +88,7 @@ int launch_probe_read(const void* buf, size_t bytes, int layout, int grid, int b
 
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
                              const void* signs_hint);
-int launch_gemm(const void* packed, int64_t N, int64_t K, const void* x, int x_bf16, int64_t M,
-                int block_len, const int8_t* signs, float* y, void* ws, hipStream_t st);
+int launch_gemm(int fmt, const void* packed, int64_t N, int64_t K, const void* x, int x_bf16,
+                int64_t M, int block_len, const int8_t* signs, float* y, void* ws, hipStream_t st);
 
 }  // namespace kq

@@ -219,16 +219,20 @@ kq_status kq_gemv_multi(kq_format fmt, int32_t nsets, const void *const *packed,
                         int32_t block_len, const int8_t *signs, float *const *y,
                         void *stream);
 
-/* Prefill GEMM (many tokens) for PQ2_0 weights, dequantize-once-per-tile
- * ([KB] "Quantized projections on the tensor units"; [BT] 8.3 tiled GEMM):
+/* Prefill GEMM (many tokens), dequantize-once-per-tile ([KB] "Quantized
+ * projections on the tensor units": each weight block becomes a bf16 tile
+ * once, then the matrix units; [BT] 8.3, the chunked prefill's tiled GEMM):
  *     y[m][n] = sum_k bf16(deq(W)[n][k]) * bf16(x'[m][k])   (fp32 accumulate)
- * x is [M][K] in x_dt (KQ_BF16 or KQ_F32); x' is rounded once to bf16;
- * y is fp32 [M][N].  Each output is within 1e-2 * sum_k |deq(W) x'| of the
- * exact value.  M >= 1, N >= 1, K % 128 == 0.  workspace: at least
- * kq_workspace_bytes(1, ...) bytes (the bf16 x').
- * Errors: as kq_gemv; KQ_EUNSUPPORTED for fmt other than KQ_FMT_PQ2_0, for
- * K > 2^21 (32-bit buffer ranges of a 256-row activation tile) or for more
- * than 2^31 - 1 output tiles. */
+ * with deq as in kq_unpack, for PQ2_0 or Q8_0 weights.  x is [M][K] in x_dt
+ * (KQ_BF16 or KQ_F32); x' (as in kq_hadamard_blocks) is rounded once to
+ * bf16; y is fp32 [M][N].  Each output is within 1e-2 * sum_k |deq(W) x'| of
+ * the exact value.  M >= 1, N >= 1, K a multiple of the block (128 or 32).
+ * The token tile follows M: 16 tokens up to M = 16, 64 up to M = 96, else
+ * 256 (a 16- or 64-token chunk does not pay for a 256-row tile).
+ * workspace: at least kq_workspace_bytes(1, ...) bytes (the bf16 x'), needed
+ * unless x is bf16 with block_len 0 and no signs.
+ * Errors: as kq_gemv; KQ_EUNSUPPORTED for K > 2^21 (32-bit buffer ranges of
+ * a 256-row activation tile) or more than 2^31 - 1 output tiles. */
 kq_status kq_gemm(kq_format fmt, const void *packed, int64_t N, int64_t K,
                   const void *x, kq_dtype x_dt, int64_t M, int32_t block_len,
                   const int8_t *signs, float *y, void *workspace,

@@ -161,7 +161,8 @@ def test_gemm_rejections():
     kq = _lib()
     g = kq.kq_gemm
     ws = 1 << 20
-    assert _status(g, 2, FAKE, 64, 128, FAKE, 1, 4, 128, None, FAKE, FAKE, ws, 0) == "KQ_EUNSUPPORTED"
+    assert _status(g, 3, FAKE, 64, 128, FAKE, 1, 4, 128, None, FAKE, FAKE, ws, 0) == "KQ_EINVAL"
+    assert _status(g, 2, FAKE, 64, 48, FAKE, 1, 4, 0, None, FAKE, FAKE, ws, 0) == "KQ_ESHAPE"
     assert _status(g, 1, FAKE, 64, 128, FAKE, 5, 4, 128, None, FAKE, FAKE, ws, 0) == "KQ_EINVAL"
     assert _status(g, 1, FAKE, 64, 96, FAKE, 1, 4, 0, None, FAKE, FAKE, ws, 0) == "KQ_ESHAPE"
     assert _status(g, 1, FAKE, 64, 128, FAKE, 1, 0, 128, None, FAKE, FAKE, ws, 0) == "KQ_ESHAPE"
