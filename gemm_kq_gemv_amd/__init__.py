@@ -11,7 +11,7 @@ built library.
 _BINDING_NAMES = (
     "kq_status_string", "kq_packed_bytes", "kq_pack_pq2", "kq_pack_q8", "kq_transcode_ptq1",
     "transcode_ptq1", "kq_unpack",
-    "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv", "kq_gemv_multi", "kq_gemm", "KQError",
+    "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv", "kq_gemv_noalloc", "kq_gemv_multi", "kq_gemm", "KQError",
     "KQ_FMT_PQ2_0", "KQ_FMT_Q8_0", "KQ_F32", "KQ_BF16", "pack", "unpack", "hadamard",
     "workspace", "gemv", "gemv_multi", "gemm", "LIB_PATH", "EXPORTS", "MAX_SETS",
     "PROBE_EXPORTS", "kq_probe_read", "kq_probe_gemv_loads",

@@ -36,7 +36,7 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_EALIGN",
 # include/kq_probe.h
 EXPORTS = ("kq_status_string", "kq_packed_bytes", "kq_pack_pq2", "kq_pack_q8",
            "kq_transcode_ptq1", "kq_unpack", "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv",
-           "kq_gemv_multi", "kq_gemm")
+           "kq_gemv_noalloc", "kq_gemv_multi", "kq_gemm")
 PROBE_EXPORTS = ("kq_probe_read", "kq_probe_gemv_loads")
 MAX_SETS = 4
 
@@ -61,6 +61,8 @@ _lib.kq_workspace_bytes.argtypes = [_i32, C.c_int, _i64, _i64, _i64, _i32, _i32]
 _lib.kq_gemv.restype = C.c_int
 _lib.kq_gemv.argtypes = [C.c_int, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p,
                          C.c_size_t, _p]
+_lib.kq_gemv_noalloc.restype = C.c_int
+_lib.kq_gemv_noalloc.argtypes = [C.c_int, _p, _i64, _i64, _p, _i64, _i32, _p, _i32, _p, _p]
 _lib.kq_gemv_multi.restype = C.c_int
 _lib.kq_gemv_multi.argtypes = [C.c_int, _i32, C.POINTER(_p), C.POINTER(_i64), _i64, _p, _i64,
                                _i32, _p, C.POINTER(_p), _p]
@@ -154,6 +156,12 @@ def kq_gemv(fmt: int, packed, N: int, K: int, x, M: int, block_len: int, signs,
     _check(_lib.kq_gemv(fmt, _ptr(packed), N, K, _ptr(x), M, block_len, _ptr(signs),
                         split_k, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)),
            "kq_gemv")
+
+
+def kq_gemv_noalloc(fmt: int, packed, N: int, K: int, x, M: int, block_len: int, signs,
+                    split_k: int, y, stream=None):
+    _check(_lib.kq_gemv_noalloc(fmt, _ptr(packed), N, K, _ptr(x), M, block_len, _ptr(signs),
+                                split_k, _ptr(y), _stream(stream)), "kq_gemv_noalloc")
 
 
 def kq_gemv_multi(fmt: int, nsets: int, packed, N, K: int, x, M: int, block_len: int, signs,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kq.h"
 #include "kq_launch.h"
 
@@ -18,6 +20,30 @@ bool shape_ok(kq_format f, int64_t N, int64_t K) {
   return N >= 1 && K >= g && K % g == 0 && N <= (int64_t(1) << 40) / K;
 }
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Scratch memory of kq_gemv_noalloc (the split-K partials), for callers that
+// cannot allocate: one static array per GPU, alive until the process ends.
+// Host code uses its per-device address from hipGetSymbolAddress, never the
+// array's name (a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];  // per device, set on its first call
+
+// Address of the current device's scratch array, resolved once per device with
+// that device current; NULL if the runtime cannot tell it.
+void* current_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
 kq_status launched(int rc) { return rc == 0 ? KQ_OK : KQ_EDEVICE; }
 
 }  // namespace
@@ -117,6 +143,28 @@ kq_status kq_gemv(kq_format fmt, const void* packed, int64_t N, int64_t K, const
   const int64_t need = kq::gemv_workspace_bytes(fmt, M, N, K, block_len, split_k);
   if (need > 0 && (!workspace || (int64_t)ws_bytes < need)) return KQ_EWORKSPACE;
   const int rc = kq::launch_gemv(fmt, packed, N, K, x, M, block_len, signs, split_k, y, workspace,
+                                 as_stream(stream));
+  return rc == -2 ? KQ_EUNSUPPORTED : launched(rc);
+}
+
+kq_status kq_gemv_noalloc(kq_format fmt, const void* packed, int64_t N, int64_t K,
+                          const float* x, int64_t M, int32_t block_len, const int8_t* signs,
+                          int32_t split_k, float* y, void* stream) {
+  if (!fmt_ok(fmt) || !packed || !x || !y) return KQ_EINVAL;
+  if (N < 0 || K < 0 || M < 0) return KQ_EINVAL;
+  if (!shape_ok(fmt, N, K) || M < 1 || M > 8 || !block_len_ok(block_len) ||
+      (block_len > 0 && K % block_len) || split_k < 0)
+    return KQ_ESHAPE;
+  if (split_k > K / kq::group_of(fmt)) return KQ_ESHAPE;
+  if (!aligned16(packed) || !aligned16(x) || !aligned16(y) || (signs && !aligned16(signs)))
+    return KQ_EALIGN;
+  kq::GemvPlan plan = kq::plan_gemv(fmt, M, N, K, block_len, split_k);
+  if (plan.split < 1) return KQ_EUNSUPPORTED;
+  const int64_t need = kq::gemv_workspace_bytes(fmt, M, N, K, block_len, split_k);
+  if (need > (int64_t)kScratchBytes) return KQ_EWORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = current_scratch())) return KQ_EDEVICE;
+  const int rc = kq::launch_gemv(fmt, packed, N, K, x, M, block_len, signs, split_k, y, ws,
                                  as_stream(stream));
   return rc == -2 ? KQ_EUNSUPPORTED : launched(rc);
 }

@@ -198,6 +198,26 @@ kq_status kq_gemv(kq_format fmt, const void *packed, int64_t N, int64_t K,
                   const int8_t *signs, int32_t split_k, float *y,
                   void *workspace, size_t ws_bytes, void *stream);
 
+/* kq_gemv for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same arguments
+ * without workspace, the same kernels and bitwise the same results.  The
+ * split-K partials, the only scratch memory kq_gemv uses, go to a static
+ * device array of the library, 8 MiB per GPU (S * M * N * 4 bytes at most,
+ * S the split kq_gemv would use; larger plans are rejected with
+ * KQ_EWORKSPACE), held by every GPU the library runs on until the process
+ * ends.  No allocation, no free, no synchronisation.  The array's address is
+ * resolved on the first call on each device, with the caller's device
+ * current (the stream must belong to it).  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams, threads)
+ * race and must be serialised by the caller; the array keeps the last call's
+ * partials, and nothing needs it to start at zero.
+ * Errors: as kq_gemv (KQ_EWORKSPACE: the plan needs more than 8 MiB;
+ * KQ_EDEVICE: the runtime could not give the array's address). */
+kq_status kq_gemv_noalloc(kq_format fmt, const void *packed, int64_t N,
+                          int64_t K, const float *x, int64_t M,
+                          int32_t block_len, const int8_t *signs,
+                          int32_t split_k, float *y, void *stream);
+
 /* Several weight sets times one activation in one launch: for s < nsets,
  *     y[s][m][n] = sum_k deq(W_s)[n][k] * x'[m][k]
  * with every W_s an N[s] x K matrix in `fmt` and x' as in kq_gemv (shared:

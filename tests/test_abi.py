@@ -157,6 +157,19 @@ def test_gemv_rejections():
 
 
 @pytest.mark.usefixtures("nogpu")
+def test_gemv_noalloc_rejections():
+    kq = _lib()
+    g = kq.kq_gemv_noalloc
+    assert _status(g, 3, FAKE, 64, 128, FAKE, 1, 128, None, 0, FAKE, 0) == "KQ_EINVAL"
+    assert _status(g, 1, FAKE, 64, 128, FAKE, 9, 128, None, 0, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 128, None, 3, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(g, 1, FAKE, 64, 256, FAKE, 1, 128, None, 0, MISALIGNED, 0) == "KQ_EALIGN"
+    assert _status(g, 1, FAKE, 64, 5120, FAKE, 1, 1024, None, 6, FAKE, 0) == "KQ_EUNSUPPORTED"
+    # partials beyond the 8 MiB scratch array: 2 x 8 x 140000 x 4 bytes
+    assert _status(g, 1, FAKE, 140000, 256, FAKE, 8, 0, None, 2, FAKE, 0) == "KQ_EWORKSPACE"
+
+
+@pytest.mark.usefixtures("nogpu")
 def test_gemm_rejections():
     kq = _lib()
     g = kq.kq_gemm
