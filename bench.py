@@ -293,12 +293,50 @@ def extras(kq, inputs, stream):
         g["mfma_util_rocprof"] = float(counters["mfma_util"])
         g["lds_bank_conflict_frac_rocprof"] = float(counters.get("lds_bank_conflict_frac", "nan"))
     out["pq2_gemm_m2048_k5120_n10240"] = g
+    # chunked-prefill token tiles at the same weights: 64- and 16-token chunks
+    for Mc in (64, 16):
+        xc = xb[:Mc].contiguous()
+        yc = torch.empty((Mc, N), device="cuda")
+        wsc, nwsc = kq.workspace(1, kq.KQ_FMT_PQ2_0, Mc, N, K, 128)
+        fns = [lambda xc=xc, yc=yc, wsc=wsc, nwsc=nwsc, Mc=Mc:
+               kq.kq_gemm(kq.KQ_FMT_PQ2_0, pg, N, K, xc, kq.KQ_BF16, Mc, 128, None, yc, wsc, nwsc)]
+        t, mad = time_fns(fns, stream, steps=40)
+        out[f"pq2_gemm_m{Mc}_k5120_n10240"] = {
+            "us_per_call": round(t * 1e6, 2), "mad_us": round(mad * 1e6, 3),
+            "TFLOPs": round(2.0 * Mc * N * K / t / 1e12, 1),
+            "weight_GBs": round(gbs(N * K // 128 * 34, t), 1)}
     # rotation pre-pass of the GEMM input, bf16 -> bf16
     xr = torch.empty_like(xb)
     fns = [lambda: kq.kq_hadamard_blocks(xb, kq.KQ_BF16, xr, kq.KQ_BF16, M, K, 128, None)]
     t, mad = time_fns(fns, stream, steps=40)
     out["hadamard_bf16_m2048_k5120"] = {"us_per_call": round(t * 1e6, 2),
                                         "GBs": round(gbs(2 * 2 * M * K, t), 1)}
+    del pg
+    torch.cuda.empty_cache()
+    # Q8_0 prefill GEMM at the FFN shape, M=2048 K=5120 N=17408 (no rotation)
+    N = 17408
+    W = torch.from_numpy(inputs.weights(1004, N, K)).cuda()
+    pq = kq.pack(kq.KQ_FMT_Q8_0, W)
+    del W
+    y = torch.empty((M, N), device="cuda")
+    fns = [lambda: kq.kq_gemm(kq.KQ_FMT_Q8_0, pq, N, K, xb, kq.KQ_BF16, M, 0, None, y, None, 0)]
+    t, mad = time_fns(fns, stream, steps=20)
+    flops = 2.0 * M * N * K
+    out["q8_gemm_m2048_k5120_n17408"] = {
+        "us_per_call": round(t * 1e6, 2), "mad_us": round(mad * 1e6, 3),
+        "TFLOPs": round(flops / t / 1e12, 1),
+        "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del pq
+    # PTQ1_0 -> PQ2_0 load-time transcode of the 5120 x 10240 weights
+    N = 10240
+    nblk = N * K // 128
+    p1 = torch.from_numpy(inputs.random_bytes(77, nblk * 28)).cuda()
+    out_p = torch.empty(kq.kq_packed_bytes(kq.KQ_FMT_PQ2_0, N, K), dtype=torch.uint8, device="cuda")
+    fns = [lambda: kq.kq_transcode_ptq1(p1, N, K, out_p)]
+    t, mad = time_fns(fns, stream, steps=40)
+    out["ptq1_transcode_k5120_n10240"] = {
+        "us_per_call": round(t * 1e6, 2),
+        "GBs": round(gbs(nblk * 28 + out_p.numel(), t), 1)}
     return out
 
 
