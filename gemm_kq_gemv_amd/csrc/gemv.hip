@@ -271,14 +271,16 @@ __device__ __forceinline__ void pair_to_operands(const uint4& v, uint2& g0, uint
 
 // The 16 2-bit codes of one word (code j at bits 2j) as signed E2M1 (fp4)
 // operands of value (c - 1) / 2: code 0 -> -0.5 (1001), 1 -> -0 (1000),
-// 2 -> +0.5 (0001), and the never-written code 3 -> +1 (0010).  Even codes go
-// to the nibbles of `ev`, odd ones to those of `od` (code 2i and 2i+1 to nibble
-// i).  Nibble bits: [3] = ~b1, [1] = b1 & b0, [0] = ~b0.  Signed operands
-// keep every product of a zero weight at zero: the matrix core sums the
-// products of one instruction aligned to the largest of them, so the smaller
-// ones keep only about 2^-17 of it, and that must be measured against the
-// output's own sum of |w x'| (a form with a constant offset added to every
-// weight lets a large activation element with a zero weight set that scale).
+// 2 -> +0.5 (0001).  Code 3 is not a PQ2_0 value (the format maps only codes
+// 0, 1 and 2, and its packer never writes 3); it becomes +0 (0000).  Even
+// codes go to the nibbles of `ev`, odd ones to those of `od` (code 2i and
+// 2i+1 to nibble i).  Nibble bits: [3] = ~b1, [2] = [1] = 0, [0] = ~b0.
+// Signed operands keep every product of a zero weight at zero: the matrix
+// core sums the products of one instruction aligned to the largest of them,
+// so the smaller ones keep only about 2^-17 of it, and that must be measured
+// against the output's own sum of |w x'| (a form with a constant offset added
+// to every weight lets a large activation element with a zero weight set that
+// scale).
 // truth table of v_bitop3_b32 for f(a, b, c): bit (a << 2 | b << 1 | c)
 template <typename F>
 constexpr uint32_t bitop3_table(F f) {
@@ -287,21 +289,18 @@ constexpr uint32_t bitop3_table(F f) {
   return t;
 }
 __device__ __forceinline__ void ternary_fp4(uint32_t w, uint32_t& ev, uint32_t& od) {
-  // p0..p3 are the bits of a nibble; M1 marks p0 and K marks p0, p1; forcing
-  // p2 of the last input to 1 makes its complement clear p2.  Nine
-  // instructions for 16 codes: two v_bitop3_b32 (any function of three
-  // inputs) per half, and the shifts and ors that line the bits up.
-  constexpr uint32_t M1 = 0x11111111u, K = 0x33333333u, P2 = 0x44444444u;
-  // m ? ~x : x & y  -- p0: ~b0, p1: b1 & b0
-  constexpr uint32_t kLow = bitop3_table([](int m, int x, int y) { return m ? !x : (x & y); });
-  // k ? x : ~y      -- p0, p1 from the first step; p2: 0, p3: ~b1
-  constexpr uint32_t kMix = bitop3_table([](int k, int x, int y) { return k ? x : !y; });
-  // even codes: b0 at p0, b1 at p1
-  const uint32_t xe = __builtin_amdgcn_bitop3_b32(M1, w, w << 1, kLow);
-  ev = __builtin_amdgcn_bitop3_b32(K, xe, (w << 2) | P2, kMix);
-  // odd codes: b0 at p2, b1 at p3
-  const uint32_t xo = __builtin_amdgcn_bitop3_b32(M1, w >> 2, w >> 1, kLow);
-  od = __builtin_amdgcn_bitop3_b32(K, xo, w | P2, kMix);
+  // p0..p3 are the bits of a nibble; M1 marks p0.  The second input carries
+  // b0 to p0, the third b1 to p3 with p1 and p2 forced to 1, so that its
+  // complement clears them.  Five instructions for 16 codes: one
+  // v_bitop3_b32 (any function of three inputs) per half, and the shifts and
+  // ors that line the bits up.
+  constexpr uint32_t M1 = 0x11111111u, P12 = 0x66666666u;
+  // m ? ~x : ~y  -- p0: ~b0; p1, p2: 0; p3: ~b1
+  constexpr uint32_t kSel = bitop3_table([](int m, int x, int y) { return m ? !x : !y; });
+  // even codes: b0 at p0, b1 at p1 (moved to p3)
+  ev = __builtin_amdgcn_bitop3_b32(M1, w, (w << 2) | P12, kSel);
+  // odd codes: b0 at p2 (moved to p0), b1 at p3
+  od = __builtin_amdgcn_bitop3_b32(M1, w >> 2, w | P12, kSel);
 }
 
 // start of part i when parts of `base` items get one more for i < rem

@@ -167,7 +167,10 @@ size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N,
  * once for all M rows):
  *     y[m][n] = sum_k deq(W)[n][k] * x'[m][k],   x' = rotation of x
  * with deq as in kq_unpack and x' as in kq_hadamard_blocks (block_len 0:
- * x' = x (.) s, no transform).  x is fp32 [M][K]; y is fp32 [M][N].
+ * x' = x (.) s, no transform), except that a PQ2_0 code 3, which is not a
+ * value of the format (only codes 0, 1, 2 are), counts as a zero weight here
+ * (kq_unpack and kq_gemm read it as 2*d).  x is fp32 [M][K]; y is fp32
+ * [M][N].
  * Arithmetic: x' in fp32, codes decoded exactly, fp32 accumulation; each
  * output is within 1e-3 * sum_k |deq(W)[n][k] x'[m][k]| of the exact value.
  * Representation limits: PQ2_0 carries each x' element as four e5m2 terms

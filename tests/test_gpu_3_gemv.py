@@ -191,6 +191,42 @@ def test_q8_rotation_blocks(M, block_len):
     assert_within_bound(_run(2, W, x, block_len, s), y_ref, b, TOL, f"q8 n={block_len} M={M}")
 
 
+@pytest.mark.parametrize("M,block_len", [(1, 128), (3, 128), (1, 1024), (5, 1024)])
+def test_code_3_is_a_zero_weight(M, block_len):
+    """Code 3 is not a PQ2_0 value (the format maps codes 0, 1 and 2); the
+    GEMV reads it as a zero weight.  A blob with random codes set to 3 gives
+    the same bits as the same blob with code 1 there, and the oracle's
+    product over the latter."""
+    kq = _kq()
+    N, K = 100, 2048
+    W = inputs.weights(1900 + M, N, K)
+    aos = oracle.pack_pq2_aos(W)
+    blk = aos.reshape(-1, 34)
+    assert not any(np.any(((blk[:, 2:] >> s_) & 3) == 3) for s_ in (0, 2, 4, 6))
+    r = inputs.rng(1901 + M)
+    nb = blk.shape[0]
+    pick_b = r.integers(0, nb, 600)
+    pick_byte = 2 + r.integers(0, 32, 600)
+    pick_sh = 2 * r.integers(0, 4, 600)
+    a3 = blk.copy()
+    for b_, c_, s_ in zip(pick_b, pick_byte, pick_sh):
+        a3[b_, c_] |= np.uint8(3 << s_)
+    a1 = a3.copy()
+    q = a1[:, 2:]
+    for s_ in (0, 2, 4, 6):
+        is3 = ((q >> s_) & 3) == 3
+        q[is3] = (q[is3] & ~np.uint8(3 << s_)) | np.uint8(1 << s_)
+    a3 = a3.reshape(-1)
+    a1 = a1.reshape(-1)
+    assert np.count_nonzero(a3 != a1) > 0
+    x = inputs.activations(1902 + M, M, K)
+    y3 = _run(1, W, x, block_len, packed=dev(oracle.aos_to_planar(1, a3, N, K)))
+    y1 = _run(1, W, x, block_len, packed=dev(oracle.aos_to_planar(1, a1, N, K)))
+    assert np.array_equal(y3.view(np.uint32), y1.view(np.uint32))
+    y_ref, b = oracle.gemv_aos(1, a1, N, K, x, block_len, None)
+    assert_within_bound(y3, y_ref, b, TOL, f"code 3, M={M}, block {block_len}")
+
+
 @pytest.mark.parametrize("fmt", [1, 2])
 @pytest.mark.parametrize("split_k", [1, 2, 3, 5, 40])
 def test_split_k(fmt, split_k):
