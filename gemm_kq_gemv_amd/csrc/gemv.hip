@@ -74,7 +74,7 @@ struct GemvSet {
   const uint8_t* dpl;
   float* out;
   int64_t N;
-  int rb_base, rb_rem;
+  int q_base, q_rem;  // row quads per workgroup of this set (see kRowUnit)
   int wg0;
   int pad;
 };
@@ -93,7 +93,7 @@ struct GemvArgs {
   int S;                 // K slices
   int total_rb;          // 16-row blocks
   int grid_x;
-  int rb_base, rb_rem;   // workgroup b owns row blocks [b*rb_base + min(b, rb_rem), next)
+  int q_base, q_rem;     // workgroup b owns row quads [b*q_base + min(b, q_rem), next)
   int u_base, u_rem;     // slice s owns rotation blocks [s*u_base + min(s, u_rem), next)
   int log2n;             // rotation block length (0: no transform)
   float inv_sqrt_n;
@@ -111,8 +111,16 @@ struct WgRows {
   const uint8_t* dpl;
   float* out;
   int64_t N;
-  int rb0, rb1;
+  int r0, r1;    // its rows [r0, r1)
+  int rb0, rb1;  // the 16-row blocks that hold them
 };
+// Rows are handed out in quads (kRowUnit rows: one 128-byte line of a
+// 16-row code tile), so that every workgroup streams the same bytes; with
+// whole 16-row blocks, 640 blocks over 256 workgroups left half of them a
+// third block (a fifth in place of 4.25 for 1088 blocks), and those set the
+// kernel's time.  A workgroup's first and last blocks may hold rows of its
+// neighbours: its lanes of those rows load nothing and write nothing.
+constexpr int kRowUnit = 4;
 __host__ __device__ __forceinline__ int part_start(int i, int base, int rem);
 // MULTI: a kernel instance for several sets (one-set calls read no set
 // fields, so their prologue starts as early as before).
@@ -125,8 +133,11 @@ __device__ __forceinline__ WgRows wg_rows(const GemvArgs& a) {
     w.dpl = a.dpl;
     w.out = a.out;
     w.N = a.N;
-    w.rb0 = part_start(b, a.rb_base, a.rb_rem);
-    w.rb1 = part_start(b + 1, a.rb_base, a.rb_rem);
+    w.r0 = kRowUnit * part_start(b, a.q_base, a.q_rem);
+    const int64_t e = (int64_t)kRowUnit * part_start(b + 1, a.q_base, a.q_rem);
+    w.r1 = (int)(e < a.N ? e : a.N);
+    w.rb0 = w.r0 / kRB;
+    w.rb1 = (w.r1 + kRB - 1) / kRB;
     return w;
   }
   const int s = (1 < a.nsets && b >= a.set[1].wg0) + (2 < a.nsets && b >= a.set[2].wg0) +
@@ -137,15 +148,27 @@ __device__ __forceinline__ WgRows wg_rows(const GemvArgs& a) {
   w.dpl = KQ_PICK(dpl);
   w.out = KQ_PICK(out);
   w.N = KQ_PICK(N);
-  const int base = KQ_PICK(rb_base), rem = KQ_PICK(rb_rem), bx = b - KQ_PICK(wg0);
+  const int base = KQ_PICK(q_base), rem = KQ_PICK(q_rem), bx = b - KQ_PICK(wg0);
 #undef KQ_PICK
-  w.rb0 = part_start(bx, base, rem);
-  w.rb1 = part_start(bx + 1, base, rem);
+  w.r0 = kRowUnit * part_start(bx, base, rem);
+  const int64_t e = (int64_t)kRowUnit * part_start(bx + 1, base, rem);
+  w.r1 = (int)(e < w.N ? e : w.N);
+  w.rb0 = w.r0 / kRB;
+  w.rb1 = (w.r1 + kRB - 1) / kRB;
   return w;
 }
 
 // ---------------------------------------------------------------------------
 // shared device helpers
+
+// The activation's address and the workgroup's weight planes as scalar
+// operands of an empty asm right after the row range is known: without it
+// the compiler loads them from the kernel arguments only where first used,
+// each behind its own wait, and the first weight loads went out about 0.4 us
+// after a wave started.
+__device__ __forceinline__ void args_in_one_batch(const GemvArgs& a, const WgRows& w) {
+  asm volatile("" ::"s"(a.x), "s"(w.qs), "s"(w.dpl));
+}
 
 __device__ __forceinline__ uint2 buffer_load_8B(BufRsrc r, uint32_t off) {
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -321,8 +344,8 @@ __device__ __forceinline__ void reduce_round(const WgRows& a, const float* part,
   for (int it = threadIdx.x; it < RBR * M * kRB; it += blockDim.x) {
     const int jr = it / (M * kRB), m = (it / kRB) % M, r = it % kRB;
     const int j = round * RBR + jr;
-    const int64_t row = (int64_t)(rb0 + j) * kRB + r;
-    if (j < nrb && row < a.N) {
+    const int row = (rb0 + j) * kRB + r;
+    if (j < nrb && row >= a.r0 && row < a.r1) {
       float t = 0.f;
       for (int w = 0; w < NW; ++w)
         for (int k = 0; k < KS; ++k) t += pr[(((w * RBR + jr) * M + m) * KS + k) * kRB + r];
@@ -464,7 +487,11 @@ __device__ __forceinline__ float group_max(float v) {
   return __uint_as_float(u);
 }
 
-template <int M, bool DALIGN, int EPL, bool MULTI>
+// FEW: every workgroup owns at most D row blocks (the host checks), so all of
+// them are in flight once the prologue has run and there is no loop.  A
+// separate instance: with the loop in the same function the compiler's
+// memory waits before the first row block covered nearly every later load.
+template <int M, bool DALIGN, int EPL, bool MULTI, bool FEW>
 __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvArgs a) {
   using C = Pq2Cfg<EPL>;
   constexpr int GS = C::GS, D = C::D, RBR = C::RBR, LPG = C::LPG;
@@ -492,6 +519,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   float* part = reinterpret_cast<float*>(lds + pq2_lds_part_offset(M, NW, GS));
 
   const WgRows wr = wg_rows<MULTI>(a);
+  args_in_one_batch(a, wr);
   const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
@@ -544,9 +572,14 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   // scales: the workgroup's whole 16-row tiles of the scale plane (padding is zero)
   const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  // this lane's row of block j, relative to the first block: inside the
+  // workgroup's rows or loaded at kFarRows (zeros, no memory touched)
+  const int rlo = wr.r0 - rb0 * kRB, rhi = wr.r1 - rb0 * kRB;
   auto issue = [&](int j, WB& b) {
-    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    const int rl = j * kRB + r16;
+    const bool mine = rl >= rlo && rl < rhi;
+    const uint32_t ro = mine ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t rod = mine ? (uint32_t)j * a.d_tile_bytes : kFarRows;
     issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gw, r16, ro, rod);
   };
   // Only the first row block is loaded before the prologue.  A wave stalls at a
@@ -758,7 +791,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     }
   };
 
-  if (nrb <= D) {
+  if constexpr (FEW) {
     // every row block is already in flight: no further loads
 #pragma unroll
     for (int i = 0; i < D; ++i)
@@ -917,6 +950,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   uint8_t* zeros = lds + q8_lds_zero_offset(M, NW, GS);
 
   const WgRows wr = wg_rows<MULTI>(a);
+  args_in_one_batch(a, wr);
   const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
@@ -959,9 +993,14 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  // this lane's row of block j, relative to the first block: inside the
+  // workgroup's rows or loaded at kFarRows (zeros, no memory touched)
+  const int rlo = wr.r0 - rb0 * kRB, rhi = wr.r1 - rb0 * kRB;
   auto issue = [&](int j, WB& b) {
-    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    const int rl = j * kRB + r16;
+    const bool mine = rl >= rlo && rl < rhi;
+    const uint32_t ro = mine ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t rod = mine ? (uint32_t)j * a.d_tile_bytes : kFarRows;
     issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gq, r16, ro, rod);
   };
 
@@ -1201,6 +1240,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
   float* part = reinterpret_cast<float*>(lds + q8b_lds_part_offset(M, NW, GS));
 
   const WgRows wr = wg_rows<MULTI>(a);
+  args_in_one_batch(a, wr);
   const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
@@ -1243,9 +1283,14 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
   const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  // this lane's row of block j, relative to the first block: inside the
+  // workgroup's rows or loaded at kFarRows (zeros, no memory touched)
+  const int rlo = wr.r0 - rb0 * kRB, rhi = wr.r1 - rb0 * kRB;
   auto issue = [&](int j, WB& b) {
-    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    const int rl = j * kRB + r16;
+    const bool mine = rl >= rlo && rl < rhi;
+    const uint32_t ro = mine ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t rod = mine ? (uint32_t)j * a.d_tile_bytes : kFarRows;
     issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gq, r16, ro, rod);
   };
 
@@ -1389,6 +1434,7 @@ __global__ __launch_bounds__(1024) void gemv_loads_twin_kernel(GemvArgs a, int M
   const int gw = g0 + wave * GS;            // first group of this wave
   const int vg = min(max(g1 - gw, 0), GS);  // its real groups
   const WgRows wr = wg_rows<false>(a);
+  args_in_one_batch(a, wr);
   const int rb0 = wr.rb0, nrb = wr.rb1 - wr.rb0;
   uint32_t acc = 0;
   // activations: the PQ2_0 kernel's lanes hold 2 GS consecutive elements of
@@ -1424,9 +1470,12 @@ __global__ __launch_bounds__(1024) void gemv_loads_twin_kernel(GemvArgs a, int M
   const uint32_t doff = (uint32_t)(gw >> 3) * 256u + (uint32_t)r16 * 16u + (uint32_t)(gw & 7) * 2u;
   const BufRsrc rq = make_rsrc(wr.qs + (int64_t)rb0 * kRB * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
   const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  const int rlo = wr.r0 - rb0 * kRB, rhi = wr.r1 - rb0 * kRB;
   auto issue = [&](int j, WBuf<GS>& b) {
-    const uint32_t ro = j < nrb ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t rod = j < nrb ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    const int rl = j * kRB + r16;
+    const bool mine = rl >= rlo && rl < rhi;
+    const uint32_t ro = mine ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t rod = mine ? (uint32_t)j * a.d_tile_bytes : kFarRows;
     issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gw, r16, ro, rod);
   };
   WBuf<GS> wb[D];
@@ -1470,6 +1519,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // host side
+
+// every workgroup of `grid` over `quads` row quads owns at most D row blocks
+// (its rows start at most 12 rows into their first block)
+static bool few_blocks(int64_t quads, int grid) {
+  const int64_t rows = (quads + grid - 1) / grid * kRowUnit;
+  static_assert(Pq2Cfg<8>::D == Pq2Cfg<16>::D, "one depth for both prologue shapes");
+  return (kRB - kRowUnit + rows + kRB - 1) / kRB <= Pq2Cfg<8>::D;
+}
 
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req) {
   GemvPlan p{};
@@ -1528,12 +1585,16 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
     }
   }
   const int NUp = G / p.units;
+  // row indices are 32-bit in the kernels
+  if (N > (int64_t(1) << 31) - 2 * kRB) return p;
   p.total_rb = (int)((N + kRB - 1) / kRB);
   const int target = kTargetWGs / S > 0 ? kTargetWGs / S : 1;
   p.grid_x = p.total_rb < target ? p.total_rb : target;
   // a workgroup's rows must fit its buffer resources (see kFarRows)
   const int64_t row_bytes = pq2 ? K / 4 : K;
-  const int64_t wg_rb = (p.total_rb + p.grid_x - 1) / p.grid_x;
+  const int64_t quads = (N + kRowUnit - 1) / kRowUnit;
+  const int64_t wg_rb = ((quads + p.grid_x - 1) / p.grid_x * kRowUnit + kRB - 1) / kRB + 1;
+  p.few = pq2 && few_blocks(quads, p.grid_x);
   if (wg_rb * kRB * row_bytes > kMaxWgBytes) {
     p.split = -1;
     return p;
@@ -1564,6 +1625,13 @@ static int launch_kernel(Kernel k, const GemvArgs& a, const GemvPlan& p, hipStre
   return 0;
 }
 
+template <int M, int EPL, bool FEW>
+static int launch_pq2(const GemvArgs& a, const GemvPlan& p, bool multi, hipStream_t st) {
+  return multi ? launch_kernel(gemv_pq2_kernel<M, true, EPL, true, FEW>, a, p, st)
+         : p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, EPL, false, FEW>, a, p, st)
+                    : launch_kernel(gemv_pq2_kernel<M, false, EPL, false, FEW>, a, p, st);
+}
+
 template <int M>
 static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
   // several sets: one K slice, so every wave starts on a whole scale run
@@ -1571,12 +1639,8 @@ static int launch_m(int fmt, const GemvArgs& a, const GemvPlan& p, hipStream_t s
   if (multi && !p.dalign) return -2;  // no launch plan for these arguments
   if (fmt == kFmtPQ2) {
     if (p.epl == 8)
-      return multi ? launch_kernel(gemv_pq2_kernel<M, true, 8, true>, a, p, st)
-             : p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 8, false>, a, p, st)
-                        : launch_kernel(gemv_pq2_kernel<M, false, 8, false>, a, p, st);
-    return multi ? launch_kernel(gemv_pq2_kernel<M, true, 16, true>, a, p, st)
-           : p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, 16, false>, a, p, st)
-                      : launch_kernel(gemv_pq2_kernel<M, false, 16, false>, a, p, st);
+      return p.few ? launch_pq2<M, 8, true>(a, p, multi, st) : launch_pq2<M, 8, false>(a, p, multi, st);
+    return p.few ? launch_pq2<M, 16, true>(a, p, multi, st) : launch_pq2<M, 16, false>(a, p, multi, st);
   }
   if (p.gs != Q8Cfg<M>::GS) return -2;
   if constexpr (M <= 4)
@@ -1638,14 +1702,18 @@ static int multi_split(int fmt, int nsets, const int64_t* N, int64_t K, int64_t 
   if (p.split != 1) return -2;
   const int64_t row_bytes = fmt == kFmtPQ2 ? K / 4 : K;
   int grid = 0;
+  bool few = fmt == kFmtPQ2;
   for (int s = 0; s < nsets; ++s) {
     const int64_t rb = (N[s] + kRB - 1) / kRB;
     int64_t w = (kTargetWGs * rb + total / 2) / total;
     w = w < 1 ? 1 : (w > rb ? rb : w);
-    if ((rb + w - 1) / w * kRB * row_bytes > kMaxWgBytes) return -2;
+    const int64_t quads = (N[s] + kRowUnit - 1) / kRowUnit;
+    if ((((quads + w - 1) / w * kRowUnit + kRB - 1) / kRB + 1) * kRB * row_bytes > kMaxWgBytes) return -2;
+    few = few && few_blocks(quads, (int)w);
     wgs[s] = (int)w;
     grid += (int)w;
   }
+  p.few = few;
   return grid;
 }
 
@@ -1670,13 +1738,13 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
     GemvSet& w = a.set[s];
     if (s < nsets) {
       const PlanarView pv = planar_view(fmt, N[s], K, const_cast<void*>(packed[s]));
-      const int rb = (int)((N[s] + kRB - 1) / kRB);
+      const int quads = (int)((N[s] + kRowUnit - 1) / kRowUnit);
       w.qs = pv.qs;
       w.dpl = pv.d;
       w.out = y[s];
       w.N = N[s];
-      w.rb_base = rb / wgs[s];
-      w.rb_rem = rb % wgs[s];
+      w.q_base = quads / wgs[s];
+      w.q_rem = quads % wgs[s];
       w.wg0 = wg0;
       wg0 += wgs[s];
     } else {
@@ -1690,8 +1758,8 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
   a.dpl = a.set[0].dpl;
   a.out = a.set[0].out;
   a.N = a.set[0].N;
-  a.rb_base = a.set[0].rb_base;
-  a.rb_rem = a.set[0].rb_rem;
+  a.q_base = a.set[0].q_base;
+  a.q_rem = a.set[0].q_rem;
   a.total_rb = 0;
   a.grid_x = grid;
   p.grid_x = grid;
@@ -1713,8 +1781,8 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
   a.N = N;
   a.total_rb = p.total_rb;
   a.grid_x = p.grid_x;
-  a.rb_base = p.total_rb / p.grid_x;
-  a.rb_rem = p.total_rb % p.grid_x;
+  a.q_base = (int)(((N + kRowUnit - 1) / kRowUnit) / p.grid_x);
+  a.q_rem = (int)(((N + kRowUnit - 1) / kRowUnit) % p.grid_x);
   float* part = p.split > 1 ? (float*)ws : nullptr;
   a.out = p.split > 1 ? part : y;
   const int rc = launch_args(fmt, a, p, M, st);
@@ -1741,8 +1809,8 @@ int launch_gemv_loads_twin(int fmt, const void* packed, int64_t N, int64_t K, co
   a.out = nullptr;
   a.total_rb = p.total_rb;
   a.grid_x = p.grid_x;
-  a.rb_base = p.total_rb / p.grid_x;
-  a.rb_rem = p.total_rb % p.grid_x;
+  a.q_base = (int)(((N + kRowUnit - 1) / kRowUnit) / p.grid_x);
+  a.q_rem = (int)(((N + kRowUnit - 1) / kRowUnit) % p.grid_x);
   const dim3 grid(p.grid_x, p.split), block(p.nw * 64);
   const int m = (int)M;
   if (fmt == kFmtPQ2) {

@@ -56,6 +56,7 @@ struct GemvPlan {
   int total_rb;   // 16-row blocks
   int lds_bytes;  // dynamic LDS per workgroup
   bool dalign;    // per-wave scale runs start on a 4-byte boundary
+  bool few;       // PQ2_0: every workgroup's row blocks are in flight at once
 };
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req);
 int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req);

@@ -194,8 +194,9 @@ size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N,
  * the block, bad block_len, split_k < 0 or larger than K's block count),
  * KQ_EALIGN, KQ_EWORKSPACE, KQ_EDEVICE; KQ_EUNSUPPORTED when no launch plan
  * fits: more K slices than rotation blocks, a K slice too wide for one
- * workgroup's LDS, or more than 512 MiB of packed codes per workgroup (a
- * workgroup streams about 1/256 of the rows). */
+ * workgroup's LDS, more than 512 MiB of packed codes per workgroup (a
+ * workgroup streams about 1/256 of the rows), or N of 2^31 - 32 rows or
+ * more. */
 kq_status kq_gemv(kq_format fmt, const void *packed, int64_t N, int64_t K,
                   const float *x, int64_t M, int32_t block_len,
                   const int8_t *signs, int32_t split_k, float *y,
