@@ -74,7 +74,7 @@ struct GemvSet {
   const uint8_t* dpl;
   float* out;
   int64_t N;
-  int q_base, q_rem;  // row quads per workgroup of this set (see kRowUnit)
+  int q_base, q_rem;  // row units per workgroup of this set (see row_unit)
   int wg0;
   int pad;
 };
@@ -93,7 +93,8 @@ struct GemvArgs {
   int S;                 // K slices
   int total_rb;          // 16-row blocks
   int grid_x;
-  int q_base, q_rem;     // workgroup b owns row quads [b*q_base + min(b, q_rem), next)
+  int q_base, q_rem;     // workgroup b owns row units [b*q_base + min(b, q_rem), next)
+  int row_unit;          // rows per unit: 4 or 16
   int u_base, u_rem;     // slice s owns rotation blocks [s*u_base + min(s, u_rem), next)
   int log2n;             // rotation block length (0: no transform)
   float inv_sqrt_n;
@@ -114,13 +115,16 @@ struct WgRows {
   int r0, r1;    // its rows [r0, r1)
   int rb0, rb1;  // the 16-row blocks that hold them
 };
-// Rows are handed out in quads (kRowUnit rows: one 128-byte line of a
-// 16-row code tile), so that every workgroup streams the same bytes; with
-// whole 16-row blocks, 640 blocks over 256 workgroups left half of them a
-// third block (a fifth in place of 4.25 for 1088 blocks), and those set the
-// kernel's time.  A workgroup's first and last blocks may hold rows of its
-// neighbours: its lanes of those rows load nothing and write nothing.
-constexpr int kRowUnit = 4;
+// Rows are handed out in units of row_unit rows.  Q8_0 uses 4 (one 128-byte
+// line of a 16-row code tile), so that every workgroup streams the same
+// bytes: with whole 16-row blocks, 1088 blocks over 256 workgroups left a
+// quarter of them a fifth block in place of 4.25, and those set the
+// kernel's time (18.5 -> 18.0 us at M = 1, 27.0 -> 26.1 us at M = 8).  A
+// workgroup's first and last blocks may then hold rows of its neighbours:
+// its lanes of those rows load nothing and write nothing.  PQ2_0 uses whole
+// blocks (16): its partial blocks cost a full block of decode and matrix
+// work for half the bytes, which measured slower (5.43 against 5.34 us at
+// 10240 rows).
 __host__ __device__ __forceinline__ int part_start(int i, int base, int rem);
 // MULTI: a kernel instance for several sets (one-set calls read no set
 // fields, so their prologue starts as early as before).
@@ -133,8 +137,8 @@ __device__ __forceinline__ WgRows wg_rows(const GemvArgs& a) {
     w.dpl = a.dpl;
     w.out = a.out;
     w.N = a.N;
-    w.r0 = kRowUnit * part_start(b, a.q_base, a.q_rem);
-    const int64_t e = (int64_t)kRowUnit * part_start(b + 1, a.q_base, a.q_rem);
+    w.r0 = a.row_unit * part_start(b, a.q_base, a.q_rem);
+    const int64_t e = (int64_t)a.row_unit * part_start(b + 1, a.q_base, a.q_rem);
     w.r1 = (int)(e < a.N ? e : a.N);
     w.rb0 = w.r0 / kRB;
     w.rb1 = (w.r1 + kRB - 1) / kRB;
@@ -150,8 +154,8 @@ __device__ __forceinline__ WgRows wg_rows(const GemvArgs& a) {
   w.N = KQ_PICK(N);
   const int base = KQ_PICK(q_base), rem = KQ_PICK(q_rem), bx = b - KQ_PICK(wg0);
 #undef KQ_PICK
-  w.r0 = kRowUnit * part_start(bx, base, rem);
-  const int64_t e = (int64_t)kRowUnit * part_start(bx + 1, base, rem);
+  w.r0 = a.row_unit * part_start(bx, base, rem);
+  const int64_t e = (int64_t)a.row_unit * part_start(bx + 1, base, rem);
   w.r1 = (int)(e < w.N ? e : w.N);
   w.rb0 = w.r0 / kRB;
   w.rb1 = (w.r1 + kRB - 1) / kRB;
@@ -1520,12 +1524,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 // host side
 
-// every workgroup of `grid` over `quads` row quads owns at most D row blocks
-// (its rows start at most 12 rows into their first block)
-static bool few_blocks(int64_t quads, int grid) {
-  const int64_t rows = (quads + grid - 1) / grid * kRowUnit;
+// rows per unit of the row split (see WgRows)
+static int row_unit(int fmt) { return fmt == kFmtPQ2 ? 16 : 4; }
+static int64_t row_units(int fmt, int64_t N) { return (N + row_unit(fmt) - 1) / row_unit(fmt); }
+// most 16-row blocks a workgroup of `grid` over `units` row units can touch
+// (its rows start at most kRB - unit rows into their first block)
+static int64_t wg_blocks(int fmt, int64_t units, int64_t grid) {
+  const int u = row_unit(fmt);
+  const int64_t rows = (units + grid - 1) / grid * u;
+  return (kRB - u + rows + kRB - 1) / kRB;
+}
+static bool few_blocks(int fmt, int64_t units, int64_t grid) {
   static_assert(Pq2Cfg<8>::D == Pq2Cfg<16>::D, "one depth for both prologue shapes");
-  return (kRB - kRowUnit + rows + kRB - 1) / kRB <= Pq2Cfg<8>::D;
+  return wg_blocks(fmt, units, grid) <= Pq2Cfg<8>::D;
 }
 
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int split_req) {
@@ -1592,9 +1603,9 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   p.grid_x = p.total_rb < target ? p.total_rb : target;
   // a workgroup's rows must fit its buffer resources (see kFarRows)
   const int64_t row_bytes = pq2 ? K / 4 : K;
-  const int64_t quads = (N + kRowUnit - 1) / kRowUnit;
-  const int64_t wg_rb = ((quads + p.grid_x - 1) / p.grid_x * kRowUnit + kRB - 1) / kRB + 1;
-  p.few = pq2 && few_blocks(quads, p.grid_x);
+  const int64_t units = row_units(fmt, N);
+  const int64_t wg_rb = wg_blocks(fmt, units, p.grid_x);
+  p.few = pq2 && few_blocks(fmt, units, p.grid_x);
   if (wg_rb * kRB * row_bytes > kMaxWgBytes) {
     p.split = -1;
     return p;
@@ -1685,6 +1696,7 @@ static void common_args(GemvArgs& a, int fmt, const GemvPlan& p, int64_t K, cons
   a.log2n = log2n;
   a.inv_sqrt_n = block_len > 1 ? (float)(1.0 / __builtin_sqrt((double)block_len)) : 1.0f;
   a.nsets = 1;
+  a.row_unit = row_unit(fmt);
 }
 
 // Workgroups per weight set: the grid of one launch (kTargetWGs) shared in
@@ -1707,9 +1719,9 @@ static int multi_split(int fmt, int nsets, const int64_t* N, int64_t K, int64_t 
     const int64_t rb = (N[s] + kRB - 1) / kRB;
     int64_t w = (kTargetWGs * rb + total / 2) / total;
     w = w < 1 ? 1 : (w > rb ? rb : w);
-    const int64_t quads = (N[s] + kRowUnit - 1) / kRowUnit;
-    if ((((quads + w - 1) / w * kRowUnit + kRB - 1) / kRB + 1) * kRB * row_bytes > kMaxWgBytes) return -2;
-    few = few && few_blocks(quads, (int)w);
+    const int64_t units = row_units(fmt, N[s]);
+    if (wg_blocks(fmt, units, w) * kRB * row_bytes > kMaxWgBytes) return -2;
+    few = few && few_blocks(fmt, units, w);
     wgs[s] = (int)w;
     grid += (int)w;
   }
@@ -1738,13 +1750,13 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
     GemvSet& w = a.set[s];
     if (s < nsets) {
       const PlanarView pv = planar_view(fmt, N[s], K, const_cast<void*>(packed[s]));
-      const int quads = (int)((N[s] + kRowUnit - 1) / kRowUnit);
+      const int units = (int)row_units(fmt, N[s]);
       w.qs = pv.qs;
       w.dpl = pv.d;
       w.out = y[s];
       w.N = N[s];
-      w.q_base = quads / wgs[s];
-      w.q_rem = quads % wgs[s];
+      w.q_base = units / wgs[s];
+      w.q_rem = units % wgs[s];
       w.wg0 = wg0;
       wg0 += wgs[s];
     } else {
@@ -1781,8 +1793,8 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
   a.N = N;
   a.total_rb = p.total_rb;
   a.grid_x = p.grid_x;
-  a.q_base = (int)(((N + kRowUnit - 1) / kRowUnit) / p.grid_x);
-  a.q_rem = (int)(((N + kRowUnit - 1) / kRowUnit) % p.grid_x);
+  a.q_base = (int)(row_units(fmt, N) / p.grid_x);
+  a.q_rem = (int)(row_units(fmt, N) % p.grid_x);
   float* part = p.split > 1 ? (float*)ws : nullptr;
   a.out = p.split > 1 ? part : y;
   const int rc = launch_args(fmt, a, p, M, st);
@@ -1809,8 +1821,8 @@ int launch_gemv_loads_twin(int fmt, const void* packed, int64_t N, int64_t K, co
   a.out = nullptr;
   a.total_rb = p.total_rb;
   a.grid_x = p.grid_x;
-  a.q_base = (int)(((N + kRowUnit - 1) / kRowUnit) / p.grid_x);
-  a.q_rem = (int)(((N + kRowUnit - 1) / kRowUnit) % p.grid_x);
+  a.q_base = (int)(row_units(fmt, N) / p.grid_x);
+  a.q_rem = (int)(row_units(fmt, N) % p.grid_x);
   const dim3 grid(p.grid_x, p.split), block(p.nw * 64);
   const int m = (int)M;
   if (fmt == kFmtPQ2) {
