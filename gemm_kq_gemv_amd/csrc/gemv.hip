@@ -216,6 +216,49 @@ __device__ __forceinline__ void lane_butterfly(float (&v)[NV]) {
   for (int i = 0; i < NV; ++i) v[i] = fmaf(sgn, v[i], xor_lane<DIST>(v[i]));
 }
 
+// The butterfly at distance 1 or 2 (inside a quad) in one instruction per
+// value: v_fmac_f32_dpp adds the partner's value times s, +1 on the lower
+// lane and -1 on the upper one, so the lower lane gets a + b and the upper
+// one b - a, the negative of the Sylvester stage's a - b.  Stages commute with
+// a sign that depends only on lane bits they do not pair, so the whole
+// transform comes out as D (H x) with D = -1 on lanes of odd parity in the
+// bits of these stages; the caller folds D into its per-element scale
+// (quad_stage_sign).  Two instructions per value (DPP move, FMA) before.
+// One asm block with its own hazard wait (a DPP read of a register written
+// by the vector ALU needs two wait states).
+template <int DIST, int NV>
+__device__ __forceinline__ void quad_butterfly(float (&v)[NV]) {
+  static_assert(DIST == 1 || DIST == 2, "quad distances");
+  static_assert(NV == 8 || NV == 16, "one block of 8 or 16 values");
+  const float s = (threadIdx.x & DIST) ? -1.f : 1.f;
+#define KQ_QB(P)                                                                          \
+  asm volatile("s_nop 1\n\t"                                                             \
+               "v_fmac_f32_dpp %0, %0, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %1, %1, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %2, %2, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %3, %3, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %4, %4, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %5, %5, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %6, %6, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %7, %7, %8 quad_perm:" P " row_mask:0xf bank_mask:0xf"      \
+               : "+v"(v[i]), "+v"(v[i + 1]), "+v"(v[i + 2]), "+v"(v[i + 3]), "+v"(v[i + 4]), \
+                 "+v"(v[i + 5]), "+v"(v[i + 6]), "+v"(v[i + 7])                             \
+               : "v"(s))
+#pragma unroll
+  for (int i = 0; i < NV; i += 8) {
+    if constexpr (DIST == 1) KQ_QB("[1,0,3,2]");
+    else KQ_QB("[2,3,0,1]");
+  }
+#undef KQ_QB
+}
+// D of quad_butterfly for a rotation of 2^log2n elements, EPL = 2^LOG_EPL per lane
+template <int LOG_EPL>
+__device__ __forceinline__ float quad_stage_sign(int log2n) {
+  const int lane = threadIdx.x;
+  const int bits = (log2n > LOG_EPL ? 1 : 0) | (log2n > LOG_EPL + 1 ? 2 : 0);
+  return (__builtin_popcount(lane & bits) & 1) ? -1.f : 1.f;
+}
+
 // The same butterfly at distance 4 or 8, where the lower and the upper lanes
 // of each pair fall in different DPP banks (groups of 4 lanes of a row): a
 // bank-masked add writes the lower lanes (partner + own) and a bank-masked
@@ -451,8 +494,8 @@ __device__ __forceinline__ void rotate_fixed(float (&v)[NV]) {
         v[i + h] = p0 - p1;
       }
   }
-  if constexpr (L > LOG_EPL) lane_butterfly<1>(v);
-  if constexpr (L > LOG_EPL + 1) lane_butterfly<2>(v);
+  if constexpr (L > LOG_EPL) quad_butterfly<1>(v);
+  if constexpr (L > LOG_EPL + 1) quad_butterfly<2>(v);
   if constexpr (L > LOG_EPL + 2) bank_butterfly<4>(v);
   if constexpr (L > LOG_EPL + 3) bank_butterfly<8>(v);
   if constexpr (L > LOG_EPL + 4) lane_butterfly<16>(v);
@@ -632,7 +675,8 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
       for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, fabsf(v[i]));
       mx = group_max<LPG>(mx);
       const int e = range_exponent(mx * a.inv_sqrt_n);
-      const float sc = ldexpf(a.inv_sqrt_n, e);
+      // (the sign of this lane's quad butterflies rides on the scale)
+      const float sc = ldexpf(a.inv_sqrt_n, e) * quad_stage_sign<C::LOG_EPL>(a.log2n);
       float r[EPL];
 #pragma unroll
       for (int i = 0; i < EPL; ++i) r[i] = v[i] = v[i] * sc;
@@ -1427,8 +1471,10 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_bf16_kernel(GemvA
 // products, no reduction.  sink[0] is written only if the XOR equals an
 // unlikely constant, so that no load can be dropped.
 
+// launch bounds of the GEMV the twin stands for (its register budget: with
+// 1024 threads the 8-group twin spilled its in-flight row blocks)
 template <bool PQ2, int GS, int D, bool DALIGN>
-__global__ __launch_bounds__(1024) void gemv_loads_twin_kernel(GemvArgs a, int M, uint32_t* sink) {
+__global__ __launch_bounds__((PQ2 ? Pq2Cfg<2 * GS>::MAXW : q8_maxw(1)) * 64) void gemv_loads_twin_kernel(GemvArgs a, int M, uint32_t* sink) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
