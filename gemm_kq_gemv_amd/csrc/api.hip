@@ -122,7 +122,7 @@ size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N, int64
     int64_t b = kq::gemv_workspace_bytes(fmt, M, N, K, block_len, split_k);
     return b < 0 ? 0 : (size_t)b;
   }
-  if (op == 1) return (size_t)kq::gemm_workspace_bytes(M, N, K, block_len, 1, nullptr);
+  if (op == 1) return (size_t)kq::gemm_workspace_bytes(fmt, M, N, K, block_len, 1, nullptr);
   return 0;
 }
 
@@ -204,8 +204,8 @@ kq_status kq_gemm(kq_format fmt, const void* packed, int64_t N, int64_t K, const
       (workspace && !aligned16(workspace)))
     return KQ_EALIGN;
   if (!kq::gemm_shape_supported(M, N, K)) return KQ_EUNSUPPORTED;
-  const int64_t need = kq::gemm_workspace_bytes(M, N, K, block_len, x_dt == KQ_BF16, signs);
-  const bool uses_ws = block_len > 0 || signs || x_dt != KQ_BF16;
+  const int64_t need = kq::gemm_workspace_bytes(fmt, M, N, K, block_len, x_dt == KQ_BF16, signs);
+  const bool uses_ws = block_len > 0 || signs || x_dt != KQ_BF16 || kq::gemm_split_count(fmt, M, N, K) > 1;
   if (uses_ws && (!workspace || (int64_t)ws_bytes < need)) return KQ_EWORKSPACE;
   return launched(kq::launch_gemm(fmt, packed, N, K, x, x_dt == KQ_BF16, M, block_len, signs, y,
                                   workspace, as_stream(stream)));

@@ -53,14 +53,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int TK = 64;
 constexpr int ROWB = TK * 2;  // bytes per LDS row (no padding)
 
-template <int FMT, int TM_, int TN_, int WGM_, int WGN_>
+template <int FMT, int TM_, int TN_, int WGM_, int WGN_, int WPC_ = 1>
 struct GemmCfg {
+  static constexpr int WPC = WPC_;  // workgroups resident per compute unit
   static constexpr int TM = TM_, TN = TN_, WGM = WGM_, WGN = WGN_;
   static_assert(WGM * WGN == 4, "four waves");
   static constexpr int WM = TM / WGM, WN = TN / WGN;   // wave tile
   static constexpr int FM = WM / 16, FN = WN / 16;     // MFMA tiles per wave
   static_assert(FM >= 1 && FN >= 1 && FM * 16 == WM && FN * 16 == WN, "whole MFMA tiles");
-  static_assert(FM >= FN, "B operands are refilled inside the A loop");
+
   static constexpr int AROWS = TM < 32 ? 32 : TM;      // LDS rows of the x' tile
   static constexpr int ALOADS = AROWS / 32;            // 16-byte x' chunks per thread
   static constexpr int UNITS = TN * TK / 8 / 256;      // 8-weight units per thread
@@ -69,6 +70,10 @@ struct GemmCfg {
   static constexpr int B_BYTES = TN * ROWB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  // K slices only for the small token tiles (gemm_split); the prompt tile
+  // keeps slice 0 as a constant (its loop scheduled slower with a run-time
+  // K range: 209 -> 277 us at 2048 x 10240 x 5120)
+  static constexpr bool SPLIT = TM < 256;
 };
 
 struct GemmArgs {
@@ -80,6 +85,9 @@ struct GemmArgs {
   int64_t d_per_row;    // blocks per row (K / 128 or K / 32)
   int64_t d_tile_bytes; // scale bytes per 16-row tile
   int mt, nt;           // tile counts
+  int S;                // K slices: workgroup b takes tile b % (mt nt), slice b / (mt nt)
+  int kt_per;           // K-tiles per slice (even for PQ2_0)
+  float* part;          // S > 1: fp32 partials [S][M][N]
 };
 
 // 8 PQ2_0 codes (16 bits, code j at bits 2j) -> 8 bf16 values (q-1)*d, as 4
@@ -124,7 +132,7 @@ __device__ __forceinline__ uint32_t load2(BufRsrc r, uint32_t off) {
 }
 
 template <typename Cfg, int FMT>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int ALOADS = Cfg::ALOADS, UNITS = Cfg::UNITS;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE_BYTES = Cfg::STAGE_BYTES;
@@ -135,8 +143,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   const int wave = tid >> 6;
   const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 
-  // ---- XCD-aware tile mapping
-  const int bid = blockIdx.x;
+  // ---- K slice and XCD-aware tile mapping
+  const int tiles = a.mt * a.nt;
+  const int slice = Cfg::SPLIT ? (int)blockIdx.x / tiles : 0;
+  const int bid = (int)blockIdx.x - slice * tiles;
   int m_tile, n_tile;
   if ((a.mt & 7) == 0) {
     // XCD x takes an eighth of the token tiles and walks every weight tile
@@ -180,8 +190,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   const uint32_t d_off = (uint32_t)((tid >> 7) * a.d_tile_bytes + ((tid >> 3) & 15) * 16);
   const uint32_t d_step = (uint32_t)(2 * a.d_tile_bytes);
   // K-tiles: PQ2_0 has an even number (K is a multiple of 128); Q8_0 may end
-  // in half a tile (K a multiple of 32), whose chunks past K load nothing
-  const int KT = (int)((a.K + TK - 1) / TK);
+  // in half a tile (K a multiple of 32), whose chunks past K load nothing.
+  // This workgroup's slice: K-tiles [kt0, kt1) (kt0 even for PQ2_0).
+  const int KTall = (int)((a.K + TK - 1) / TK);
+  const int kt0 = Cfg::SPLIT ? slice * a.kt_per : 0;
+  const int kt1 = Cfg::SPLIT && kt0 + a.kt_per < KTall ? kt0 + a.kt_per : KTall;
+  const int KT = kt1 - kt0;
 
   // LDS byte offset of this thread's 16-byte chunk in rows arow + 32 i:
   // row * 128 + (chunk ^ (row / 2) % 8) * 16, and (row / 2) % 8 = (t / 16) % 8
@@ -194,9 +208,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   uint32_t rq[PQ2 ? UNITS : 1];
   uint2 rq8[PQ2 ? 1 : UNITS];
   uint32_t rdd[UNITS];
-  auto gload = [&](int kt) {
-    // the prefetches of the last two iterations load nothing
-    const bool in_k = PQ2 ? kt < KT : (int64_t)kt * TK + 8 * achunk < a.K;
+  auto gload = [&](int t) {
+    // absolute K-tile; the prefetches of the last two iterations load nothing
+    const int kt = kt0 + t;
+    const bool in_k = PQ2 ? kt < kt1 : kt < kt1 && (int64_t)kt * TK + 8 * achunk < a.K;
 #pragma unroll
     for (int i = 0; i < ALOADS; ++i) {
       const uint32_t ak = PQ2 ? a_off + (uint32_t)(((kt >> 1) * 128 + (kt & 1) * 8) * 2)
@@ -277,6 +292,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
       fa[i] = lda(ns, nks, i);
       if (i < FN) fb[cur ^ 1][i] = ldb(ns, nks, i);
     }
+#pragma unroll
+    for (int j = FM; j < FN; ++j) fb[cur ^ 1][j] = ldb(ns, nks, j);
   };
   // scheduling hints for the 256 x 160 tile: spread the staging (loads,
   // dequantization, LDS writes) between its MFMAs
@@ -351,6 +368,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   }
 
   // ---- epilogue: lane (j, q), register r -> row 4q + r, column j of a tile
+  float* out = Cfg::SPLIT && a.S > 1 ? a.part + (int64_t)slice * a.M * a.N : a.y;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -359,7 +377,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + r;
-        if (row < a.M && col < a.N) a.y[row * a.N + col] = acc[i][j][r];
+        if (row < a.M && col < a.N) out[row * a.N + col] = acc[i][j][r];
       }
     }
   }
@@ -373,21 +391,51 @@ template <int FMT> using Cfg16 = GemmCfg<FMT, 16, 64, 1, 4>;
 
 // token tile for M tokens: 16 up to 16, 64 up to 96, else 256
 static int gemm_tile_m(int64_t M) { return M <= 16 ? 16 : (M <= 96 ? 64 : 256); }
+static int gemm_tile_n(int tm) { return tm == 256 ? 160 : 64; }
+
+// K slices of the small token tiles.  A 16- or 64-token tile has little work
+// per K-tile, so its loop waits on memory each K-tile; the N / 64 tiles of one
+// chunk leave most compute units idle.  Splitting K until there are up to
+// four workgroups per compute unit (1024: one round, as four 64-token
+// workgroups fit a compute unit), in slices of whole K-tile pairs for PQ2_0,
+// gives each workgroup about a sixth of the loop; the fp32 partials are
+// added in slice order by a second kernel (deterministic).
+struct GemmSplit {
+  int S, kt_per;
+};
+static GemmSplit gemm_split(int fmt, int64_t M, int64_t N, int64_t K) {
+  const int tm = gemm_tile_m(M), tn = gemm_tile_n(tm);
+  const int64_t KT = (K + TK - 1) / TK;
+  const int64_t tiles = ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+  if (tm == 256 || tiles >= 1024) return {1, (int)KT};
+  const int unit = fmt == kFmtPQ2 ? 2 : 1;
+  const int64_t units = (KT + unit - 1) / unit;
+  int64_t S = 1024 / tiles;
+  S = S < units ? S : units;
+  S = S < 16 ? S : 16;
+  const int64_t kt_per = (units + S - 1) / S * unit;
+  return {(int)((KT + kt_per - 1) / kt_per), (int)kt_per};
+}
 
 // 32-bit buffer ranges and offsets: a 256-row x' tile spans 512 K bytes,
 // which must stay below the out-of-range offset (kOutOfRange, about 2^31);
 // the tile grid must fit an int.
 bool gemm_shape_supported(int64_t M, int64_t N, int64_t K) {
   if (K > kGemmMaxK) return false;
-  const int tm = gemm_tile_m(M), tn = tm == 256 ? 160 : 64;
+  const int tm = gemm_tile_m(M), tn = gemm_tile_n(tm);
   const int64_t mt = (M + tm - 1) / tm, nt = (N + tn - 1) / tn;
   return mt * nt <= 0x7FFFFFFF;
 }
 
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
+int gemm_split_count(int fmt, int64_t M, int64_t N, int64_t K) { return gemm_split(fmt, M, N, K).S; }
+
+// x' (bf16 [M][K], 256-byte aligned), then the split partials (fp32 [S][M][N])
+static int64_t gemm_xb_bytes(int64_t M, int64_t K) { return (M * K * 2 + 255) / 256 * 256; }
+int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
                              const void* signs_hint) {
-  (void)N; (void)block_len; (void)x_bf16; (void)signs_hint;
-  return (M * K * 2 + 255) / 256 * 256;
+  (void)block_len; (void)x_bf16; (void)signs_hint;
+  const GemmSplit sp = gemm_split(fmt, M, N, K);
+  return gemm_xb_bytes(M, K) + (sp.S > 1 ? (int64_t)sp.S * M * N * 4 : 0);
 }
 
 template <typename Cfg, int FMT>
@@ -402,8 +450,9 @@ static int launch_tile(const GemmArgs& base, hipStream_t st) {
       hipFuncSetAttribute((const void*)gemm_kernel<Cfg, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           Cfg::LDS_BYTES) == hipSuccess;
   if (!attr_ok) return -1;
-  gemm_kernel<Cfg, FMT><<<a.mt * a.nt, 256, Cfg::LDS_BYTES, st>>>(a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  gemm_kernel<Cfg, FMT><<<a.mt * a.nt * a.S, 256, Cfg::LDS_BYTES, st>>>(a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  return a.S > 1 ? launch_splitk_reduce(a.part, a.y, a.M * a.N, a.S, st) : 0;
 }
 
 template <int FMT>
@@ -434,6 +483,10 @@ int launch_gemm(int fmt, const void* packed, int64_t N, int64_t K, const void* x
   a.d_per_row = pv.d_per_row;
   a.d_tile_bytes = pv.d_tile_bytes;
   a.mt = a.nt = 0;
+  const GemmSplit sp = gemm_split(fmt, M, N, K);
+  a.S = sp.S;
+  a.kt_per = sp.kt_per;
+  a.part = sp.S > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + gemm_xb_bytes(M, K)) : nullptr;
   return fmt == kFmtPQ2 ? launch_fmt<kFmtPQ2>(a, st) : launch_fmt<kFmtQ8>(a, st);
 }
 

@@ -1572,6 +1572,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 // host side
 
+int launch_splitk_reduce(const float* part, float* y, int64_t n, int S, hipStream_t st) {
+  if (n <= 0) return 0;
+  splitk_reduce_kernel<<<(int)((n + 255) / 256), 256, 0, st>>>(part, y, n, S);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // rows per unit of the row split (see WgRows)
 static int row_unit(int fmt) { return fmt == kFmtPQ2 ? 16 : 4; }
 static int64_t row_units(int fmt, int64_t N) { return (N + row_unit(fmt) - 1) / row_unit(fmt); }

@@ -87,8 +87,12 @@ int launch_gemv_loads_twin(int fmt, const void* packed, int64_t N, int64_t K, co
 int launch_probe_read(const void* buf, size_t bytes, int layout, int grid, int block,
                       uint32_t* sink, hipStream_t st);
 
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
+int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int x_bf16,
                              const void* signs_hint);
+// K slices of the GEMM (1: one pass; more: fp32 partials in the workspace)
+int gemm_split_count(int fmt, int64_t M, int64_t N, int64_t K);
+// y[i] = sum_{s < S} part[s n + i], ascending s (the GEMV's split-K reduce)
+int launch_splitk_reduce(const float* part, float* y, int64_t n, int S, hipStream_t st);
 int launch_gemm(int fmt, const void* packed, int64_t N, int64_t K, const void* x, int x_bf16,
                 int64_t M, int block_len, const int8_t* signs, float* y, void* ws, hipStream_t st);
 

@@ -252,9 +252,14 @@ kq_status kq_gemv_multi(kq_format fmt, int32_t nsets, const void *const *packed,
  * bf16; y is fp32 [M][N].  Each output is within 1e-2 * sum_k |deq(W) x'| of
  * the exact value.  M >= 1, N >= 1, K a multiple of the block (128 or 32).
  * The token tile follows M: 16 tokens up to M = 16, 64 up to M = 96, else
- * 256 (a 16- or 64-token chunk does not pay for a 256-row tile).
- * workspace: at least kq_workspace_bytes(1, ...) bytes (the bf16 x'), needed
- * unless x is bf16 with block_len 0 and no signs.
+ * 256 (a 16- or 64-token chunk does not pay for a 256-row tile).  With the
+ * 16- and 64-token tiles K is split into slices (about 1024 workgroups in
+ * all), whose fp32 partial products are added in slice order: the result is
+ * bitwise reproducible for a given (M, N, K).
+ * workspace: at least kq_workspace_bytes(1, ...) bytes (room for the bf16 x',
+ * then the slices' fp32 partials [S][M][N]); needed when x' is staged
+ * (block_len > 0, signs, or fp32 x) or K is split (the 16- and 64-token tiles
+ * when there are fewer than 1024 output tiles), else it may be NULL.
  * Errors: as kq_gemv; KQ_EUNSUPPORTED for K > 2^21 (32-bit buffer ranges of
  * a 256-row activation tile) or more than 2^31 - 1 output tiles. */
 kq_status kq_gemm(kq_format fmt, const void *packed, int64_t N, int64_t K,

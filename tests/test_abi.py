@@ -70,6 +70,8 @@ def test_workspace_sizes():
     # more slices than rotation blocks: no plan
     assert kq.kq_workspace_bytes(0, 1, 1, 10240, 5120, 1024, 6) == 0
     assert kq.kq_workspace_bytes(1, 1, 2048, 10240, 5120, 128, 0) == 2048 * 5120 * 2
+    # a 16-token chunk splits K in 6 slices of 14 K-tiles: x' then the partials
+    assert kq.kq_workspace_bytes(1, 1, 16, 10240, 5120, 128, 0) == 16 * 5120 * 2 + 6 * 16 * 10240 * 4
     assert kq.kq_workspace_bytes(0, 1, 9, 64, 128, 0, 0) == 0   # M > 8
     assert kq.kq_workspace_bytes(0, 1, 1, 64, 100, 0, 0) == 0   # bad K
 

@@ -8,7 +8,9 @@ kernel issues (x' chunks, PQ2_0 code words and scales, Q8_0 code pairs and
 scales) for the three token tiles, and checks at tail shapes (M % TM, N % TN,
 M = 1, a Q8_0 K ending in half a K-tile) that every load either reads exactly
 the element it stands for, inside its resource, or sits at or past the end of
-the resource (so the hardware returns zeros without touching memory)."""
+the resource (so the hardware returns zeros without touching memory).  The
+16- and 64-token tiles split K into slices of whole K-tiles (pairs for
+PQ2_0); each slice's loads are checked over its own K-tiles and prefetches."""
 import pytest
 
 OOR = 0x7FFFFFF0
@@ -18,6 +20,21 @@ CFGS = {256: (256, 160), 64: (64, 64), 16: (16, 64)}
 
 def tile_m(M):
     return 16 if M <= 16 else (64 if M <= 96 else 256)
+
+
+def k_slices(fmt, M, N, K):
+    """(first, end) K-tiles of each slice: the small tiles are split into up
+    to 1024 workgroups, in units of 2 K-tiles for PQ2_0."""
+    TM, TN = CFGS[tile_m(M)]
+    KT = -(-K // TK)
+    tiles = -(-M // TM) * -(-N // TN)
+    if TM == 256 or tiles >= 1024:
+        return [(0, KT)]
+    unit = 2 if fmt == 1 else 1
+    units = -(-KT // unit)
+    S = max(1, min(1024 // tiles, units, 16))
+    per = -(-units // S) * unit
+    return [(k0, min(k0 + per, KT)) for k0 in range(0, KT, per)]
 
 
 def check(fmt, M, N, K):
@@ -41,8 +58,9 @@ def check(fmt, M, N, K):
             for tid in range(256):
                 arow, ach = tid >> 3, tid & 7
                 a_off = (arow * K + ach * (16 if fmt == 1 else 8)) * 2
-                for kt in range(KT + 2):            # the kernel prefetches two tiles ahead
-                    in_k = kt < KT if fmt == 1 else kt * TK + 8 * ach < K
+                for kt0, kt1 in k_slices(fmt, M, N, K):
+                  for kt in range(kt0, kt1 + 2):    # the kernel prefetches two tiles ahead
+                    in_k = kt < kt1 if fmt == 1 else kt < kt1 and kt * TK + 8 * ach < K
                     for i in range(ALOADS):
                         row = 32 * i + arow
                         if fmt == 1:
@@ -97,6 +115,18 @@ def check(fmt, M, N, K):
 @pytest.mark.parametrize("fmt,M,N,K", [
     (1, 1, 1, 128), (1, 300, 170, 640), (1, 2048, 10240, 256), (1, 17, 65, 384), (1, 97, 161, 128),
     (1, 64, 64, 256), (2, 1, 1, 32), (2, 300, 170, 96), (2, 70, 17, 160), (2, 16, 100, 224),
-    (2, 257, 161, 352)])
+    (2, 257, 161, 352), (1, 16, 640, 5120), (2, 64, 640, 1056), (1, 96, 130, 2048)])
 def test_gemm_loads_stay_in_range(fmt, M, N, K):
     check(fmt, M, N, K)
+
+
+def test_k_slices_cover_k_once():
+    for fmt, M, N, K in ((1, 16, 10240, 5120), (1, 64, 10240, 5120), (2, 16, 17408, 5120),
+                         (2, 5, 100, 96), (1, 96, 130, 2048), (1, 1, 1, 128)):
+        sl = k_slices(fmt, M, N, K)
+        KT = -(-K // TK)
+        assert sl[0][0] == 0 and sl[-1][1] == KT
+        assert all(a[1] == b[0] for a, b in zip(sl, sl[1:]))
+        assert all(k1 > k0 for k0, k1 in sl)
+        if fmt == 1:
+            assert all(k0 % 2 == 0 for k0, _ in sl)
