@@ -1653,7 +1653,14 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   // row indices are 32-bit in the kernels
   if (N > (int64_t(1) << 31) - 2 * kRB) return p;
   p.total_rb = (int)((N + kRB - 1) / kRB);
-  const int target = kTargetWGs / S > 0 ? kTargetWGs / S : 1;
+  // PQ2_0: every K slice gets the whole grid.  Its waves need at most 168
+  // VGPRs, so a compute unit holds two slices' 5-wave workgroups (S = 2) or
+  // four 3-wave ones (S = 4), and a split adds waves instead of thinning them
+  // (248320 rows: S = 2 64.8 -> 58.4 us, S = 4 99.6 -> 62.7).  Q8_0 keeps one
+  // grid in total, which measured faster (17408 rows, M = 4, S = 2: 25.0 against
+  // 31.8 us; M = 8: 26.1 against 34.6, whose 256-VGPR waves leave room for one
+  // 5-wave workgroup per compute unit).
+  const int target = pq2 ? kTargetWGs : (kTargetWGs / S > 0 ? kTargetWGs / S : 1);
   p.grid_x = p.total_rb < target ? p.total_rb : target;
   // a workgroup's rows must fit its buffer resources (see kFarRows)
   const int64_t row_bytes = pq2 ? K / 4 : K;
