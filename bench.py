@@ -274,6 +274,20 @@ def extras(kq, inputs, stream):
             "us_loads_only_twin": round(tw * 1e6, 2)}
     del heads, ph
     torch.cuda.empty_cache()
+    # reachable bf16 MFMA rate: the GEMM's instruction issued from registers,
+    # the best of a few launch shapes, about 0.55 TFLOP per launch; the first
+    # shape has the GEMM's occupancy (one wave per SIMD)
+    ceiling = {}
+    for grid, block in ((256, 256), (256, 512), (512, 512), (1024, 256)):
+        iters = 2048 * 1024 // (grid * block // 64)
+        fns = [lambda g=grid, b=block, i=iters: kq.kq_probe_mfma(i, g, b, sink)]
+        t, _ = time_fns(fns, stream, steps=20)
+        ceiling[(grid, block)] = grid * (block // 64) * iters * 16 * 16384 / t / 1e12
+    (cg, cb), mfma_tf = max(ceiling.items(), key=lambda kv: kv[1])
+    out["mfma_bf16_16x16x32_ceiling"] = {
+        "TFLOPs": round(mfma_tf, 1), "frac_bf16_peak": round(mfma_tf / BF16_PEAK_TFLOPS, 4),
+        "grid": cg, "block": cb,
+        "TFLOPs_one_wave_per_simd": round(ceiling[(256, 256)], 1)}
     # PQ2_0 prefill GEMM M=2048 K=5120 N=10240 (bf16 MFMA)
     M, N = 2048, 10240
     W = torch.from_numpy(inputs.weights(1005, N, K)).cuda()
@@ -287,7 +301,8 @@ def extras(kq, inputs, stream):
     flops = 2.0 * M * N * K
     g = {"us_per_call": round(t * 1e6, 2), "mad_us": round(mad * 1e6, 3),
          "TFLOPs": round(flops / t / 1e12, 1),
-         "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+         "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+         "frac_mfma_ceiling": round(flops / t / 1e12 / mfma_tf, 4)}
     counters = profile_fields("gemm_pq2_m2048_k5120_n10240_counters.txt", gemm_sha())
     if counters:
         g["mfma_util_rocprof"] = float(counters["mfma_util"])
@@ -325,7 +340,8 @@ def extras(kq, inputs, stream):
     out["q8_gemm_m2048_k5120_n17408"] = {
         "us_per_call": round(t * 1e6, 2), "mad_us": round(mad * 1e6, 3),
         "TFLOPs": round(flops / t / 1e12, 1),
-        "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        "frac_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "frac_mfma_ceiling": round(flops / t / 1e12 / mfma_tf, 4)}
     del pq
     # PTQ1_0 -> PQ2_0 load-time transcode of the 5120 x 10240 weights
     N = 10240

@@ -14,7 +14,7 @@ _BINDING_NAMES = (
     "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv", "kq_gemv_noalloc", "kq_gemv_multi", "kq_gemm", "KQError",
     "KQ_FMT_PQ2_0", "KQ_FMT_Q8_0", "KQ_F32", "KQ_BF16", "pack", "unpack", "hadamard",
     "workspace", "gemv", "gemv_multi", "gemm", "LIB_PATH", "EXPORTS", "MAX_SETS",
-    "PROBE_EXPORTS", "kq_probe_read", "kq_probe_gemv_loads",
+    "PROBE_EXPORTS", "kq_probe_read", "kq_probe_mfma", "kq_probe_gemv_loads",
 )
 
 

@@ -37,7 +37,7 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_EALIGN",
 EXPORTS = ("kq_status_string", "kq_packed_bytes", "kq_pack_pq2", "kq_pack_q8",
            "kq_transcode_ptq1", "kq_unpack", "kq_hadamard_blocks", "kq_workspace_bytes", "kq_gemv",
            "kq_gemv_noalloc", "kq_gemv_multi", "kq_gemm")
-PROBE_EXPORTS = ("kq_probe_read", "kq_probe_gemv_loads")
+PROBE_EXPORTS = ("kq_probe_read", "kq_probe_mfma", "kq_probe_gemv_loads")
 MAX_SETS = 4
 
 _p = C.c_void_p
@@ -71,6 +71,8 @@ _lib.kq_gemm.argtypes = [C.c_int, _p, _i64, _i64, _p, C.c_int, _i64, _i32, _p, _
                          C.c_size_t, _p]
 _lib.kq_probe_read.restype = C.c_int
 _lib.kq_probe_read.argtypes = [_p, C.c_size_t, _i32, _i32, _i32, _p, _p]
+_lib.kq_probe_mfma.restype = C.c_int
+_lib.kq_probe_mfma.argtypes = [_i32, _i32, _i32, _p, _p]
 _lib.kq_probe_gemv_loads.restype = C.c_int
 _lib.kq_probe_gemv_loads.argtypes = [C.c_int, _p, _i64, _i64, _p, _i64, _i32, _i32, _p, _p]
 
@@ -183,6 +185,10 @@ def kq_gemm(fmt: int, packed, N: int, K: int, x, x_dt: int, M: int, block_len: i
 def kq_probe_read(buf, nbytes: int, layout: int, grid: int, block: int, sink, stream=None):
     _check(_lib.kq_probe_read(_ptr(buf), nbytes, layout, grid, block, _ptr(sink),
                               _stream(stream)), "kq_probe_read")
+
+
+def kq_probe_mfma(iters: int, grid: int, block: int, sink, stream=None):
+    _check(_lib.kq_probe_mfma(iters, grid, block, _ptr(sink), _stream(stream)), "kq_probe_mfma")
 
 
 def kq_probe_gemv_loads(fmt: int, packed, N: int, K: int, x, M: int, block_len: int,

@@ -1,7 +1,8 @@
 // probe.hip -- measurement instruments (include/kq_probe.h): a streaming
-// read-reduce, the reachable HBM read rate on this GPU, and the entry point
-// of the GEMV's loads-only twin (its kernel sits beside the GEMV kernels, so
-// that both use the same row-block load code).
+// read-reduce, the reachable HBM read rate on this GPU; a matrix-core issue
+// loop, the reachable bf16 MFMA rate; and the entry point of the GEMV's
+// loads-only twin (its kernel sits beside the GEMV kernels, so that both use
+// the same row-block load code).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,6 +58,39 @@ int launch_probe_read(const void* buf, size_t bytes, int layout, int grid, int b
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// Matrix-core issue ceiling: every wave runs `iters` rounds of kChains
+// independent v_mfma_f32_16x16x32_bf16 (the prefill GEMM's instruction) on
+// operands held in registers, and only then sums its accumulators.  The
+// operand values are small multiples of 1/16, so the sums stay finite.
+constexpr int kMfmaChains = 16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(1024) void probe_mfma_kernel(int iters, uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.0625f * (float)((lane + i) & 3));
+    b[i] = (__bf16)(0.0625f * (float)((lane + 2 * i) & 3));
+  }
+  f32x4 acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) s += (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);
+  if (__float_as_uint(s) == 0x9E3779B9u) sink[0] = __float_as_uint(s);
+}
+
+int launch_probe_mfma(int iters, int grid, int block, uint32_t* sink, hipStream_t st) {
+  hipLaunchKernelGGL(probe_mfma_kernel, dim3(grid), dim3(block), 0, st, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace kq
 
 namespace {
@@ -75,6 +109,16 @@ kq_status kq_probe_read(const void* buf, size_t bytes, int32_t layout, int32_t g
   return kq::launch_probe_read(buf, bytes, layout, grid, block, sink, (hipStream_t)stream) == 0
              ? KQ_OK
              : KQ_EDEVICE;
+}
+
+kq_status kq_probe_mfma(int32_t iters, int32_t grid, int32_t block, uint32_t* sink, void* stream) {
+  if (!sink) return KQ_EINVAL;
+  if (iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536 || block < 64 || block > 1024 ||
+      block % 64)
+    return KQ_ESHAPE;
+  if (!aligned16(sink)) return KQ_EALIGN;
+  return kq::launch_probe_mfma(iters, grid, block, sink, (hipStream_t)stream) == 0 ? KQ_OK
+                                                                                   : KQ_EDEVICE;
 }
 
 kq_status kq_probe_gemv_loads(kq_format fmt, const void* packed, int64_t N, int64_t K,

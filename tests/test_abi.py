@@ -199,6 +199,13 @@ def test_probe_rejections():
     assert _status(r, FAKE, 1024, 0, 256, 96, FAKE, 0) == "KQ_ESHAPE"
     assert _status(r, FAKE, 1000, 0, 256, 256, FAKE, 0) == "KQ_ESHAPE"
     assert _status(r, MISALIGNED, 1024, 0, 256, 256, FAKE, 0) == "KQ_EALIGN"
+    m = kq.kq_probe_mfma
+    assert _status(m, 16, 256, 256, None, 0) == "KQ_EINVAL"
+    assert _status(m, 0, 256, 256, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(m, (1 << 20) + 1, 256, 256, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(m, 16, 0, 256, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(m, 16, 256, 1088, FAKE, 0) == "KQ_ESHAPE"
+    assert _status(m, 16, 256, 256, MISALIGNED, 0) == "KQ_EALIGN"
     t = kq.kq_probe_gemv_loads
     assert _status(t, 3, FAKE, 64, 128, FAKE, 1, 128, 0, FAKE, 0) == "KQ_EINVAL"
     assert _status(t, 1, FAKE, 64, 192, FAKE, 1, 128, 0, FAKE, 0) == "KQ_ESHAPE"

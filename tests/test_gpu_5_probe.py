@@ -46,3 +46,14 @@ def test_gemv_loads_twin(fmt, M, bl, S):
     with pytest.raises(kq.KQError) as e:
         kq.kq_probe_gemv_loads(fmt, packed, N, K, x, M, bl, K // (128 if fmt == 1 else 32) + 1, sink)
     assert e.value.name == "KQ_ESHAPE"
+
+
+@pytest.mark.parametrize("iters,grid,block", [(1, 1, 64), (64, 256, 256), (8, 37, 1024)])
+def test_probe_mfma(iters, grid, block):
+    kq = _kq()
+    sink = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    kq.kq_probe_mfma(iters, grid, block, sink)
+    assert np.all(host(sink) == -7)
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_probe_mfma(iters, grid, 96, sink)
+    assert e.value.name == "KQ_ESHAPE"
