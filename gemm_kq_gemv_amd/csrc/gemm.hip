@@ -42,6 +42,7 @@
 //   token tiles and walk every weight tile over it, so the x' rows stay in
 //   that XCD's L2 while the weight tiles stream past.
 #include <type_traits>
+#include <utility>
 
 #include "kq_device.h"
 #include "kq_launch.h"
@@ -111,6 +112,16 @@ __device__ __forceinline__ uint4 dequant8_q8(uint2 w, float d) {
   }
   return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                     pack_bf16x2(v[6], v[7]));
+}
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // buffer loads with the whole offset per lane (range-checked)
@@ -208,53 +219,58 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   uint32_t rq[PQ2 ? UNITS : 1];
   uint2 rq8[PQ2 ? 1 : UNITS];
   uint32_t rdd[UNITS];
-  auto gload = [&](int t) {
+  // the staging in pieces: x' chunk i and weight unit i of a K-tile
+  auto gload_a = [&](int t, int i) __attribute__((always_inline)) {
     // absolute K-tile; the prefetches of the last two iterations load nothing
     const int kt = kt0 + t;
     const bool in_k = PQ2 ? kt < kt1 : kt < kt1 && (int64_t)kt * TK + 8 * achunk < a.K;
-#pragma unroll
-    for (int i = 0; i < ALOADS; ++i) {
-      const uint32_t ak = PQ2 ? a_off + (uint32_t)(((kt >> 1) * 128 + (kt & 1) * 8) * 2)
-                              : a_off + (uint32_t)(kt * TK * 2);
-      // rows past TM (the 16-token tile stages 32 LDS rows) load nothing
-      const bool in_m = 32 * i + arow < TM;
-      ra[i] = load16(ra_rs, in_k && in_m ? ak + i * rowstep : kOutOfRange);
-    }
+    const uint32_t ak = PQ2 ? a_off + (uint32_t)(((kt >> 1) * 128 + (kt & 1) * 8) * 2)
+                            : a_off + (uint32_t)(kt * TK * 2);
+    // rows past TM (the 16-token tile stages 32 LDS rows) load nothing
+    const bool in_m = 32 * i + arow < TM;
+    ra[i] = load16(ra_rs, in_k && in_m ? ak + i * rowstep : kOutOfRange);
+  };
+  auto gload_b = [&](int t, int i) __attribute__((always_inline)) {
+    const int kt = kt0 + t;
+    const bool in_k = PQ2 ? kt < kt1 : kt < kt1 && (int64_t)kt * TK + 8 * achunk < a.K;
     if constexpr (PQ2) {
       if ((kt & 1) == 0) {
         const uint32_t kb = (uint32_t)kt >> 1;
         const uint32_t qk = q_off + kb * 512;
         const uint32_t dk = d_off + (kb >> 3) * 256 + (kb & 7) * 2;
-#pragma unroll
-        for (int i = 0; i < UNITS; ++i) {
-          rq[i] = load4(rq_rs, in_k ? qk + i * q_step : kOutOfRange);
-          rdd[i] = load2(rd_rs, in_k ? dk + i * d_step : kOutOfRange);
-        }
+        rq[i] = load4(rq_rs, in_k ? qk + i * q_step : kOutOfRange);
+        rdd[i] = load2(rd_rs, in_k ? dk + i * d_step : kOutOfRange);
       }
     } else {
       // the unit's 32-block: 2 kt + chunk / 4
       const uint32_t b = 2u * (uint32_t)kt + ((uint32_t)achunk >> 2);
       const uint32_t qk = q_off + (uint32_t)kt * 1024u;
       const uint32_t dk = d_off + (b >> 3) * 256 + (b & 7) * 2;
-#pragma unroll
-      for (int i = 0; i < UNITS; ++i) {
-        rq8[i] = load8(rq_rs, in_k ? qk + i * q_step : kOutOfRange);
-        rdd[i] = load2(rd_rs, in_k ? dk + i * d_step : kOutOfRange);
-      }
+      rq8[i] = load8(rq_rs, in_k ? qk + i * q_step : kOutOfRange);
+      rdd[i] = load2(rd_rs, in_k ? dk + i * d_step : kOutOfRange);
     }
   };
-  auto sstore = [&](int stage, int kt) {
-    uint8_t* S = smem + stage * STAGE_BYTES;
+  auto gload = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < ALOADS; ++i) *reinterpret_cast<uint4*>(S + w_lds + i * 32 * ROWB) = ra[i];
+    for (int i = 0; i < ALOADS; ++i) gload_a(t, i);
 #pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      const float d = f16_bits_to_f32(rdd[i]);
-      uint4 v;
-      if constexpr (PQ2) v = dequant8_pq2(rq[i] >> (16 * (kt & 1)), d);
-      else v = dequant8_q8(rq8[i], d);
-      *reinterpret_cast<uint4*>(S + A_BYTES + w_lds + i * 32 * ROWB) = v;
-    }
+    for (int i = 0; i < UNITS; ++i) gload_b(t, i);
+  };
+  auto sstore_a = [&](int stage, int i) __attribute__((always_inline)) {
+    *reinterpret_cast<uint4*>(smem + stage * STAGE_BYTES + w_lds + i * 32 * ROWB) = ra[i];
+  };
+  auto sstore_b = [&](int stage, int kt, int i) __attribute__((always_inline)) {
+    const float d = f16_bits_to_f32(rdd[i]);
+    uint4 v;
+    if constexpr (PQ2) v = dequant8_pq2(rq[i] >> (16 * (kt & 1)), d);
+    else v = dequant8_q8(rq8[i], d);
+    *reinterpret_cast<uint4*>(smem + stage * STAGE_BYTES + A_BYTES + w_lds + i * 32 * ROWB) = v;
+  };
+  auto sstore = [&](int stage, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < ALOADS; ++i) sstore_a(stage, i);
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) sstore_b(stage, kt, i);
   };
 
   f32x4 acc[FM][FN];
@@ -275,15 +291,15 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   // one set of A operands, refilled row tile by row tile as the MFMAs release
   // them; two sets of B operands (all are used by every row tile)
   bf16x8 fa[FM], fb[2][FN];
-  auto lda = [&](int stage, int ks, int i) {
+  auto lda = [&](int stage, int ks, int i) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8*>(smem + stage * STAGE_BYTES + (ks ? a_rd1 : a_rd0) + i * 16 * ROWB);
   };
-  auto ldb = [&](int stage, int ks, int j) {
+  auto ldb = [&](int stage, int ks, int j) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8*>(smem + stage * STAGE_BYTES + (ks ? b_rd1 : b_rd0) + j * 16 * ROWB);
   };
   // the MFMAs of one k-step with B set `cur`, reading the operands of the next
   // k-step (stage `ns`, k-step `nks`) into A and B set `cur ^ 1`
-  auto mma = [&](int cur, int ns, int nks) {
+  auto mma = [&](int cur, int ns, int nks) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -297,7 +313,7 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   };
   // scheduling hints for the 256 x 160 tile: spread the staging (loads,
   // dequantization, LDS writes) between its MFMAs
-  auto hints0 = [&]() {
+  auto hints0 = [&]() __attribute__((always_inline)) {
     if constexpr (FM == 8 && FN == 5) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -311,7 +327,7 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
       }
     }
   };
-  auto hints1 = [&]() {
+  auto hints1 = [&]() __attribute__((always_inline)) {
     if constexpr (FM == 8 && FN == 5) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -340,13 +356,39 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   // Second half, after the barrier: k-step 1 while the next tile's k-step 0 is
   // read.  The other stage was last read before the previous barrier, so one
   // barrier per tile suffices.
-  auto iter = [&](int t, auto STAGE) {
+  // k-step 0 of the 256 x 160 tile with the staging cut into its rows: after
+  // the MFMAs of row tile i and the reads of its next operands, x' chunk i and
+  // weight unit i of tile t + 1 go to LDS and those of tile t + 2 are fetched
+  auto half0_staged = [&](int st, int t) __attribute__((always_inline)) {
+    static_for<FM>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[0][j], acc[i][j], 0, 0, 0);
+      fa[i] = lda(st, 1, i);
+      if constexpr (i < FN) fb[1][i] = ldb(st, 1, i);
+      if constexpr (i < ALOADS) {
+        sstore_a(st ^ 1, i);
+        gload_a(t + 2, i);
+      }
+      if constexpr (i < UNITS) {
+        sstore_b(st ^ 1, t + 1, i);
+        gload_b(t + 2, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto iter = [&](int t, auto STAGE) __attribute__((always_inline)) {
     constexpr int st = decltype(STAGE)::value;
     __builtin_amdgcn_sched_barrier(0);
-    sstore(st ^ 1, t + 1);
-    gload(t + 2);
-    mma(0, st, 1);
-    hints0();
+    if constexpr (FM == 8 && FN == 5) {
+      half0_staged(st, t);
+    } else {
+      sstore(st ^ 1, t + 1);
+      gload(t + 2);
+      mma(0, st, 1);
+      hints0();
+    }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     mma(1, st ^ 1, 0);
