@@ -10,11 +10,14 @@
 //
 // gfx950 design
 // -------------
-// * Block tiles TM (tokens) x TN (weight rows) x 64 (K), 4 waves in a
+// * Block tiles TM (tokens) x TN (weight rows) x 64 (K), 4 or 8 waves in a
 //   WGM x WGN arrangement, each wave owning (TM / WGM) x (TN / WGN) outputs as
 //   v_mfma_f32_16x16x32_bf16 accumulators.  Three instances:
-//     256 x 160, waves 2 x 2 (128 x 80 each, 40 accumulators): prompts; at
-//       M = 2048, N = 10240 that is 512 tiles, two per CU, with no tail;
+//     256 x 160, 8 waves 4 x 2 (64 x 80 each, 20 accumulators): prompts; at
+//       M = 2048, N = 10240 that is 512 tiles, two per CU, with no tail.  Two
+//       waves per SIMD: while one waits on LDS or a barrier the other issues
+//       its MFMAs (with 4 waves of 128 x 80 the matrix cores were busy 42.5%
+//       of the time, and the kernel ran 204 us against 188);
 //     64 x 64 and 16 x 64, waves 1 x 4 (one 16-column slice each): the
 //       64- and 16-token chunks of a chunked prefill, where a 256-token tile
 //       would spend 3/4 or 15/16 of its matrix-core work on padding rows.
@@ -58,15 +61,22 @@ template <int FMT, int TM_, int TN_, int WGM_, int WGN_, int WPC_ = 1>
 struct GemmCfg {
   static constexpr int WPC = WPC_;  // workgroups resident per compute unit
   static constexpr int TM = TM_, TN = TN_, WGM = WGM_, WGN = WGN_;
-  static_assert(WGM * WGN == 4, "four waves");
+  static constexpr int NW = WGM * WGN;                 // waves
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static constexpr int NT = 64 * NW;                   // threads
+  static constexpr int RPP = NT / 8;                   // LDS rows staged per pass (8 chunks a row)
   static constexpr int WM = TM / WGM, WN = TN / WGN;   // wave tile
   static constexpr int FM = WM / 16, FN = WN / 16;     // MFMA tiles per wave
   static_assert(FM >= 1 && FN >= 1 && FM * 16 == WM && FN * 16 == WN, "whole MFMA tiles");
 
   static constexpr int AROWS = TM < 32 ? 32 : TM;      // LDS rows of the x' tile
-  static constexpr int ALOADS = AROWS / 32;            // 16-byte x' chunks per thread
-  static constexpr int UNITS = TN * TK / 8 / 256;      // 8-weight units per thread
-  static_assert(TN * TK / 8 == UNITS * 256, "units must divide evenly");
+  static_assert(AROWS % RPP == 0, "whole passes of x' rows");
+  static constexpr int ALOADS = AROWS / RPP;           // 16-byte x' chunks per thread
+  // 8-weight units per thread; the last pass may cover only the first
+  // UNIT_TAIL threads (whole waves)
+  static constexpr int UNITS = (TN * TK / 8 + NT - 1) / NT;
+  static constexpr int UNIT_TAIL = TN * TK / 8 - (UNITS - 1) * NT;
+  static_assert(UNIT_TAIL % 64 == 0 && TN % 16 == 0 && RPP % 16 == 0, "whole waves, 16-row tiles");
   static constexpr int A_BYTES = AROWS * ROWB;
   static constexpr int B_BYTES = TN * ROWB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -143,9 +153,9 @@ __device__ __forceinline__ uint32_t load2(BufRsrc r, uint32_t off) {
 }
 
 template <typename Cfg, int FMT>
-__global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(Cfg::NT, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WM = Cfg::WM, WN = Cfg::WN, FM = Cfg::FM, FN = Cfg::FN;
-  constexpr int ALOADS = Cfg::ALOADS, UNITS = Cfg::UNITS;
+  constexpr int ALOADS = Cfg::ALOADS, UNITS = Cfg::UNITS, RPP = Cfg::RPP;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE_BYTES = Cfg::STAGE_BYTES;
   constexpr bool PQ2 = FMT == kFmtPQ2;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -177,7 +187,8 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   const int64_t m0 = (int64_t)m_tile * TM, n0 = (int64_t)n_tile * TN;
 
   // ---- global load geometry.  Thread t stages x' chunk t % 8 (8 bf16) of
-  // rows t / 8 + 32 i, and weight units (rows t / 8 + 32 i, chunk t % 8).
+  // rows t / 8 + RPP i, and weight units (rows t / 8 + RPP i, chunk t % 8),
+  // RPP = threads / 8 rows a pass.
   // K order inside a tile: PQ2_0 interleaves the two K-tiles of a 128-block in
   // runs of 8 (chunk c of K-tile 2b + h holds elements 16 c + 8 h .. + 7 of
   // block b), so that one 4-byte word per unit brings a thread's codes for
@@ -192,14 +203,14 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   const BufRsrc rq_rs = make_rsrc(a.qs + (n0 >> 4) * G * 512, (uint32_t)((brows + 15) / 16 * G * 512));
   const BufRsrc rd_rs = make_rsrc(a.dpl + (n0 >> 4) * a.d_tile_bytes, (uint32_t)((brows + 15) / 16 * a.d_tile_bytes));
   const uint32_t a_off = (uint32_t)(arow * a.K + achunk * (PQ2 ? 16 : 8)) * 2u;
-  const uint32_t rowstep = (uint32_t)(32 * a.K * 2);
-  // unit i: weight row 32 i + t / 8 = 16-row tile (t / 128 + 2 i), row (t / 8) % 16
+  const uint32_t rowstep = (uint32_t)(RPP * a.K * 2);
+  // unit i: weight row RPP i + t / 8 = 16-row tile (t / 128 + RPP / 16 i), row (t / 8) % 16
   const uint32_t q_off = PQ2 ? (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + achunk * 4)
                              : (uint32_t)((tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + (achunk & 3) * 8 +
                                           (achunk >> 2) * 512);
-  const uint32_t q_step = (uint32_t)(2 * G * 512);  // two 16-row tiles
+  const uint32_t q_step = (uint32_t)(RPP / 16 * G * 512);  // a pass of 16-row tiles
   const uint32_t d_off = (uint32_t)((tid >> 7) * a.d_tile_bytes + ((tid >> 3) & 15) * 16);
-  const uint32_t d_step = (uint32_t)(2 * a.d_tile_bytes);
+  const uint32_t d_step = (uint32_t)(RPP / 16 * a.d_tile_bytes);
   // K-tiles: PQ2_0 has an even number (K is a multiple of 128); Q8_0 may end
   // in half a tile (K a multiple of 32), whose chunks past K load nothing.
   // This workgroup's slice: K-tiles [kt0, kt1) (kt0 even for PQ2_0).
@@ -208,7 +219,7 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   const int kt1 = Cfg::SPLIT && kt0 + a.kt_per < KTall ? kt0 + a.kt_per : KTall;
   const int KT = kt1 - kt0;
 
-  // LDS byte offset of this thread's 16-byte chunk in rows arow + 32 i:
+  // LDS byte offset of this thread's 16-byte chunk in rows arow + RPP i:
   // row * 128 + (chunk ^ (row / 2) % 8) * 16, and (row / 2) % 8 = (t / 16) % 8
   const uint32_t w_lds = (uint32_t)(arow * ROWB + ((achunk ^ ((tid >> 4) & 7)) << 4));
 
@@ -227,12 +238,16 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
     const uint32_t ak = PQ2 ? a_off + (uint32_t)(((kt >> 1) * 128 + (kt & 1) * 8) * 2)
                             : a_off + (uint32_t)(kt * TK * 2);
     // rows past TM (the 16-token tile stages 32 LDS rows) load nothing
-    const bool in_m = 32 * i + arow < TM;
+    const bool in_m = RPP * i + arow < TM;
     ra[i] = load16(ra_rs, in_k && in_m ? ak + i * rowstep : kOutOfRange);
+  };
+  // the last pass of weight units covers the first UNIT_TAIL threads
+  auto unit_ok = [&](int i) __attribute__((always_inline)) {
+    return Cfg::UNIT_TAIL == Cfg::NT || i < UNITS - 1 || tid < Cfg::UNIT_TAIL;
   };
   auto gload_b = [&](int t, int i) __attribute__((always_inline)) {
     const int kt = kt0 + t;
-    const bool in_k = PQ2 ? kt < kt1 : kt < kt1 && (int64_t)kt * TK + 8 * achunk < a.K;
+    const bool in_k = (PQ2 ? kt < kt1 : kt < kt1 && (int64_t)kt * TK + 8 * achunk < a.K) && unit_ok(i);
     if constexpr (PQ2) {
       if ((kt & 1) == 0) {
         const uint32_t kb = (uint32_t)kt >> 1;
@@ -257,14 +272,15 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < UNITS; ++i) gload_b(t, i);
   };
   auto sstore_a = [&](int stage, int i) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(smem + stage * STAGE_BYTES + w_lds + i * 32 * ROWB) = ra[i];
+    *reinterpret_cast<uint4*>(smem + stage * STAGE_BYTES + w_lds + i * RPP * ROWB) = ra[i];
   };
   auto sstore_b = [&](int stage, int kt, int i) __attribute__((always_inline)) {
+    if (!unit_ok(i)) return;
     const float d = f16_bits_to_f32(rdd[i]);
     uint4 v;
     if constexpr (PQ2) v = dequant8_pq2(rq[i] >> (16 * (kt & 1)), d);
     else v = dequant8_q8(rq8[i], d);
-    *reinterpret_cast<uint4*>(smem + stage * STAGE_BYTES + A_BYTES + w_lds + i * 32 * ROWB) = v;
+    *reinterpret_cast<uint4*>(smem + stage * STAGE_BYTES + A_BYTES + w_lds + i * RPP * ROWB) = v;
   };
   auto sstore = [&](int stage, int kt) __attribute__((always_inline)) {
 #pragma unroll
@@ -307,38 +323,11 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cur][j], acc[i][j], 0, 0, 0);
       fa[i] = lda(ns, nks, i);
       if (i < FN) fb[cur ^ 1][i] = ldb(ns, nks, i);
+      // B operands past the last row tile are read with the first ones
+      if (FM + i < FN) fb[cur ^ 1][FM + i] = ldb(ns, nks, FM + i);
     }
-#pragma unroll
-    for (int j = FM; j < FN; ++j) fb[cur ^ 1][j] = ldb(ns, nks, j);
+    static_assert(FN <= 2 * FM, "every B operand read in a row tile");
   };
-  // scheduling hints for the 256 x 160 tile: spread the staging (loads,
-  // dequantization, LDS writes) between its MFMAs
-  auto hints0 = [&]() __attribute__((always_inline)) {
-    if constexpr (FM == 8 && FN == 5) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (j == 1 || j == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        }
-        if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-  };
-  auto hints1 = [&]() __attribute__((always_inline)) {
-    if constexpr (FM == 8 && FN == 5) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-  };
-
   // prologue: tiles 0 and 1 to stages 0 and 1, tiles 2 and 3 in flight,
   // the first k-step's operands in registers
   gload(0);
@@ -367,6 +356,7 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[0][j], acc[i][j], 0, 0, 0);
       fa[i] = lda(st, 1, i);
       if constexpr (i < FN) fb[1][i] = ldb(st, 1, i);
+      if constexpr (FM + i < FN) fb[1][FM + i] = ldb(st, 1, FM + i);
       if constexpr (i < ALOADS) {
         sstore_a(st ^ 1, i);
         gload_a(t + 2, i);
@@ -381,18 +371,17 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
   auto iter = [&](int t, auto STAGE) __attribute__((always_inline)) {
     constexpr int st = decltype(STAGE)::value;
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (FM == 8 && FN == 5) {
+    if constexpr (TM == 256) {
+      static_assert(FM >= ALOADS && FM >= UNITS, "a staging piece per row tile");
       half0_staged(st, t);
     } else {
       sstore(st ^ 1, t + 1);
       gload(t + 2);
       mma(0, st, 1);
-      hints0();
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     mma(1, st ^ 1, 0);
-    hints1();
     __builtin_amdgcn_sched_barrier(0);
   };
   // the last tiles are peeled off the loop: with them inside, the compiler
@@ -427,7 +416,7 @@ __global__ __launch_bounds__(256, Cfg::WPC) void gemm_kernel(GemmArgs a) {
 
 // Token-tile instances: the 256 x 160 prompt tile, and 64- / 16-token tiles
 // of 64 weight rows for short chunks.
-template <int FMT> using CfgBig = GemmCfg<FMT, 256, 160, 2, 2>;
+template <int FMT> using CfgBig = GemmCfg<FMT, 256, 160, 4, 2>;
 template <int FMT> using Cfg64 = GemmCfg<FMT, 64, 64, 1, 4>;
 template <int FMT> using Cfg16 = GemmCfg<FMT, 16, 64, 1, 4>;
 
@@ -492,7 +481,7 @@ static int launch_tile(const GemmArgs& base, hipStream_t st) {
       hipFuncSetAttribute((const void*)gemm_kernel<Cfg, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           Cfg::LDS_BYTES) == hipSuccess;
   if (!attr_ok) return -1;
-  gemm_kernel<Cfg, FMT><<<a.mt * a.nt * a.S, 256, Cfg::LDS_BYTES, st>>>(a);
+  gemm_kernel<Cfg, FMT><<<a.mt * a.nt * a.S, Cfg::NT, Cfg::LDS_BYTES, st>>>(a);
   if (hipGetLastError() != hipSuccess) return -1;
   return a.S > 1 ? launch_splitk_reduce(a.part, a.y, a.M * a.N, a.S, st) : 0;
 }

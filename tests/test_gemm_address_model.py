@@ -15,7 +15,7 @@ import pytest
 
 OOR = 0x7FFFFFF0
 TK = 64
-CFGS = {256: (256, 160), 64: (64, 64), 16: (16, 64)}
+CFGS = {256: (256, 160, 512), 64: (64, 64, 256), 16: (16, 64, 256)}  # TM: (TM, TN, threads)
 
 
 def tile_m(M):
@@ -25,7 +25,7 @@ def tile_m(M):
 def k_slices(fmt, M, N, K):
     """(first, end) K-tiles of each slice: the small tiles are split into up
     to 1024 workgroups, in units of 2 K-tiles for PQ2_0."""
-    TM, TN = CFGS[tile_m(M)]
+    TM, TN, _ = CFGS[tile_m(M)]
     KT = -(-K // TK)
     tiles = -(-M // TM) * -(-N // TN)
     if TM == 256 or tiles >= 1024:
@@ -38,9 +38,13 @@ def k_slices(fmt, M, N, K):
 
 
 def check(fmt, M, N, K):
-    TM, TN = CFGS[tile_m(M)]
+    TM, TN, NT = CFGS[tile_m(M)]
+    RPP = NT // 8                      # rows staged per pass
     AROWS = max(TM, 32)
-    ALOADS, UNITS = AROWS // 32, TN * TK // 8 // 256
+    ALOADS = AROWS // RPP
+    UNITS = -(-(TN * TK // 8) // NT)   # the last pass covers the first UNIT_TAIL threads
+    UNIT_TAIL = TN * TK // 8 - (UNITS - 1) * NT
+    assert AROWS % RPP == 0 and UNIT_TAIL % 64 == 0
     group = 128 if fmt == 1 else 32
     G = K // group
     C = (G + 7) // 8
@@ -55,27 +59,27 @@ def check(fmt, M, N, K):
             q_size = -(-brows // 16) * G * 512
             d_size = -(-brows // 16) * d_tile
             assert max(a_size, q_size, d_size) < OOR
-            for tid in range(256):
+            for tid in range(NT):
                 arow, ach = tid >> 3, tid & 7
                 a_off = (arow * K + ach * (16 if fmt == 1 else 8)) * 2
                 for kt0, kt1 in k_slices(fmt, M, N, K):
                   for kt in range(kt0, kt1 + 2):    # the kernel prefetches two tiles ahead
                     in_k = kt < kt1 if fmt == 1 else kt < kt1 and kt * TK + 8 * ach < K
                     for i in range(ALOADS):
-                        row = 32 * i + arow
+                        row = RPP * i + arow
                         if fmt == 1:
                             k = (kt >> 1) * 128 + (kt & 1) * 8 + 16 * ach
                             ak = a_off + ((kt >> 1) * 128 + (kt & 1) * 8) * 2
                         else:
                             k = kt * TK + 8 * ach
                             ak = a_off + kt * TK * 2
-                        off = ak + i * 32 * K * 2 if (in_k and row < TM) else OOR
+                        off = ak + i * RPP * K * 2 if (in_k and row < TM) else OOR
                         valid = in_k and row < TM and row < arows and k < K
                         if valid:
                             assert off == (row * K + k) * 2 and off + 16 <= a_size
                         else:
                             assert off >= a_size, (fmt, M, N, K, tid, kt, i)
-                    # weight units: row 32 i + t / 8, chunk t % 8
+                    # weight units: row RPP i + t / 8, chunk t % 8
                     if fmt == 1:
                         if kt % 2:
                             continue                  # a block's words come with its even K-tile
@@ -83,10 +87,13 @@ def check(fmt, M, N, K):
                         q_off = (tid >> 7) * G * 512 + ((tid >> 3) & 15) * 32 + ach * 4
                         d_off = (tid >> 7) * d_tile + ((tid >> 3) & 15) * 16
                         for i in range(UNITS):
-                            row = 32 * i + (tid >> 3)
-                            qo = q_off + kb * 512 + i * 2 * G * 512 if in_k else OOR
-                            do = d_off + (kb >> 3) * 256 + (kb & 7) * 2 + i * 2 * 256 * C if in_k else OOR
-                            if in_k and row < -(-brows // 16) * 16:
+                            row = RPP * i + (tid >> 3)
+                            ok = in_k and (i < UNITS - 1 or tid < UNIT_TAIL)
+                            qo = q_off + kb * 512 + i * (RPP // 16) * G * 512 if ok else OOR
+                            do = d_off + (kb >> 3) * 256 + (kb & 7) * 2 + i * (RPP // 16) * 256 * C if ok else OOR
+                            if ok:
+                                assert row < TN
+                            if ok and row < -(-brows // 16) * 16:
                                 assert qo == ((row // 16) * G + kb) * 512 + (row % 16) * 32 + ach * 4
                                 assert qo + 4 <= q_size
                                 assert do == ((row // 16) * C + kb // 8) * 256 + (row % 16) * 16 + 2 * (kb % 8)
@@ -99,10 +106,13 @@ def check(fmt, M, N, K):
                                  + (ach >> 2) * 512)
                         d_off = (tid >> 7) * d_tile + ((tid >> 3) & 15) * 16
                         for i in range(UNITS):
-                            row = 32 * i + (tid >> 3)
-                            qo = q_off + kt * 1024 + i * 2 * G * 512 if in_k else OOR
-                            do = (d_off + (b >> 3) * 256 + (b & 7) * 2 + i * 2 * 256 * C) if in_k else OOR
-                            if in_k and row < -(-brows // 16) * 16:
+                            row = RPP * i + (tid >> 3)
+                            ok = in_k and (i < UNITS - 1 or tid < UNIT_TAIL)
+                            qo = q_off + kt * 1024 + i * (RPP // 16) * G * 512 if ok else OOR
+                            do = (d_off + (b >> 3) * 256 + (b & 7) * 2 + i * (RPP // 16) * 256 * C) if ok else OOR
+                            if ok:
+                                assert row < TN
+                            if ok and row < -(-brows // 16) * 16:
                                 assert b < G
                                 assert qo == ((row // 16) * G + b) * 512 + (row % 16) * 32 + (ach & 3) * 8
                                 assert qo + 8 <= q_size
