@@ -69,7 +69,7 @@ struct GemmCfg {
   static constexpr int FM = WM / 16, FN = WN / 16;     // MFMA tiles per wave
   static_assert(FM >= 1 && FN >= 1 && FM * 16 == WM && FN * 16 == WN, "whole MFMA tiles");
 
-  static constexpr int AROWS = TM < 32 ? 32 : TM;      // LDS rows of the x' tile
+  static constexpr int AROWS = TM < RPP ? RPP : TM;    // LDS rows of the x' tile (a whole pass)
   static_assert(AROWS % RPP == 0, "whole passes of x' rows");
   static constexpr int ALOADS = AROWS / RPP;           // 16-byte x' chunks per thread
   // 8-weight units per thread; the last pass may cover only the first
