@@ -448,6 +448,29 @@ __device__ __forceinline__ void issue_row_block(WBuf<GS>& b, BufRsrc rq, BufRsrc
   }
 }
 
+// The same loads in parts, for a buffer that is refilled while it is read:
+// the codes of pair q, and the scales of groups 8c .. 8c + 7 (whole aligned
+// runs, DALIGN) or of pair c alone (otherwise).
+template <int GS>
+__device__ __forceinline__ void issue_codes(WBuf<GS>& b, int q, BufRsrc rq, uint32_t qo, uint32_t ro) {
+  b.q[q] = buffer_load_16B_stream(rq, qo + ro);
+}
+template <int GS, bool DALIGN>
+__device__ __forceinline__ void issue_scales(WBuf<GS>& b, int c, BufRsrc rd, uint32_t doff, int gfirst,
+                                             int r16, uint32_t rod) {
+  if constexpr (DALIGN) {
+    static_assert(GS >= 8, "scale runs of eight groups");
+    const uint4 t = buffer_load_16B(rd, doff + rod + 256u * c);
+    b.d[4 * c] = t.x; b.d[4 * c + 1] = t.y; b.d[4 * c + 2] = t.z; b.d[4 * c + 3] = t.w;
+  } else {
+    const uint32_t rbase = (uint32_t)r16 * 16u + rod;
+    const int ge = gfirst + 2 * c, go = ge + 1;
+    const uint32_t oe = (uint32_t)(ge >> 3) * 256u + (uint32_t)(ge & 7) * 2u;
+    const uint32_t oo = (uint32_t)(go >> 3) * 256u + (uint32_t)(go & 7) * 2u;
+    b.d[c] = buffer_load_2B(rd, rbase + oe) | (buffer_load_2B(rd, rbase + oo) << 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // PQ2_0
 
@@ -868,16 +891,17 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 //
 // The int8 weights are the B operand of v_mfma_i32_16x16x32_i8 as loaded.  x'
 // is scaled per activation row (over the workgroup's K slice) by a power of two
-// 2^s that puts its largest magnitude in [32, 64), and written as four int8
-// digits: v = x' 2^s, q0 = rne(v), r0 = v - q0, q(t+1) = rne(128 rt),
-// r(t+1) = 128 rt - q(t+1).  Every digit lies in [-64, 64], and
-// x' 2^s = sum_t qt 2^(-7t) to within 2^-22, i.e. 2^-27 of the row's largest
-// magnitude.  Operand row 4t + m holds digit t of activation row m, so lane
-// block kb ends with digit kb of every row; each group's integer sum (below
-// 32*127*64 in magnitude) converts to fp32 exactly and is scaled by the group's
-// fp16 d with one fma_mix.  The digit weight 2^(-7kb) and 2^-s are applied once
-// per row block, and the four lane blocks' partials are added by the LDS
-// reduction in a fixed order.
+// 2^s that puts its largest magnitude in [2^29, 2^30), rounded to an integer
+// I = rne(x' 2^s) (within 1/2, i.e. 2^-30 of the row's largest magnitude), and
+// written as four signed base-256 digits, most significant first:
+// I = sum_t d_t 256^(3-t) with every d_t in [-128, 127].  J = I + 0x80808080 is
+// non-negative and its bytes are d_t + 128 (base-256 digits of J), so the
+// digits are J's bytes with their top bit flipped.  Operand row 4t + m holds
+// digit t of activation row m, so lane block kb ends with digit kb of every
+// row; each group's integer sum (below 32*127*128 in magnitude) converts to fp32
+// exactly and is scaled by the group's fp16 d.  The digit weight 256^(3-kb)
+// and 2^-s are applied once per row block, and the four lane blocks' partials
+// are added by the LDS reduction in a fixed order.
 
 // 16 groups of 32 per wave (two chunks of scales).  Row blocks of weight loads
 // in flight: two for one activation row, one for two to four (their digit
@@ -957,20 +981,27 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
   return __uint_as_float(u);
 }
 
-// exponent s that puts bound * 2^s in [32, 64), within [-126, 126] so that 2^s and
-// 2^-s stay finite (0 for a zero, infinite or NaN bound)
+// exponent s that puts bound * 2^s in [2^29, 2^30), within [-126, 126] so that 2^s
+// and 2^-s stay finite (0 for a zero, infinite or NaN bound)
 __device__ __forceinline__ int digit_exponent(float bound) {
   const uint32_t ef = (__float_as_uint(bound) >> 23) & 0xFFu;
   if (!(bound > 0.f) || ef == 0xFFu) return 0;
-  const int e = 5 - ((int)ef - 127);
+  const int e = 29 - ((int)ef - 127);
   return e < -126 ? -126 : (e > 126 ? 126 : e);
 }
 
-// low bytes of four words, in order, as one word
-__device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
-  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // [b0.0, b1.0, 0, 0]
-  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  // [b2.0, b3.0, 0, 0]
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);               // [lo.0, lo.1, hi.0, hi.1]
+// 4 x 4 byte transpose: out[k] = [j0.k, j1.k, j2.k, j3.k] (byte k of each word,
+// in order), eight v_perm_b32
+__device__ __forceinline__ void transpose_bytes(uint32_t j0, uint32_t j1, uint32_t j2, uint32_t j3,
+                                                uint32_t (&out)[4]) {
+  const uint32_t p_lo = __builtin_amdgcn_perm(j1, j0, 0x05010400u);  // [j0.0, j1.0, j0.1, j1.1]
+  const uint32_t p_hi = __builtin_amdgcn_perm(j1, j0, 0x07030602u);  // [j0.2, j1.2, j0.3, j1.3]
+  const uint32_t q_lo = __builtin_amdgcn_perm(j3, j2, 0x05010400u);
+  const uint32_t q_hi = __builtin_amdgcn_perm(j3, j2, 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(q_lo, p_lo, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(q_lo, p_lo, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(q_hi, p_hi, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(q_hi, p_hi, 0x07060302u);
 }
 
 template <int M, bool DALIGN, bool MULTI>
@@ -1140,34 +1171,22 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
     ysc[m] = ldexpf(1.f, -e);
   }
   {
-    // adding 1.5 * 2^23 rounds a float of magnitude below 2^22 to the nearest
-    // integer (ties to even) and leaves it, two's complement, in the low bits
-    const float kRound = 12582912.f;
+    constexpr uint32_t kBias = 0x80808080u;
     for (int c = tid; c < nch; c += blockDim.x) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float4* ptr = reinterpret_cast<float4*>(xs + m * KRmax + 8 * c);
         const float4 f0 = ptr[0], f1 = ptr[1];
-        float v[8] = {f0.x * cs[m], f0.y * cs[m], f0.z * cs[m], f0.w * cs[m],
-                      f1.x * cs[m], f1.y * cs[m], f1.z * cs[m], f1.w * cs[m]};
-        uint32_t dg[4][2];
+        const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        uint32_t J[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uint32_t bits[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float u = v[i] + kRound;
-            bits[i] = __float_as_uint(u);
-            // next residual 128 (v - q), q = u - kRound: -128 q and 128 (v - q)
-            // are exact, so two fused steps give the same bits as subtract,
-            // subtract, multiply
-            if (t < 3) v[i] = fmaf(v[i], 128.f, fmaf(u, -128.f, 128.f * kRound));
-          }
-          dg[t][0] = low_bytes(bits[0], bits[1], bits[2], bits[3]);
-          dg[t][1] = low_bytes(bits[4], bits[5], bits[6], bits[7]);
-        }
-        ptr[0] = __builtin_bit_cast(float4, make_uint4(dg[0][0], dg[0][1], dg[1][0], dg[1][1]));
-        ptr[1] = __builtin_bit_cast(float4, make_uint4(dg[2][0], dg[2][1], dg[3][0], dg[3][1]));
+        for (int i = 0; i < 8; ++i) J[i] = (uint32_t)(int)__builtin_rintf(v[i] * cs[m]) + kBias;
+        // plane t (digit t) is byte 3 - t of each J, top bit flipped
+        uint32_t lo[4], hi[4];
+        transpose_bytes(J[0], J[1], J[2], J[3], lo);
+        transpose_bytes(J[4], J[5], J[6], J[7], hi);
+        ptr[0] = __builtin_bit_cast(float4, make_uint4(lo[3] ^ kBias, hi[3] ^ kBias, lo[2] ^ kBias, hi[2] ^ kBias));
+        ptr[1] = __builtin_bit_cast(float4, make_uint4(lo[1] ^ kBias, hi[1] ^ kBias, lo[0] ^ kBias, hi[0] ^ kBias));
       }
     }
   }
@@ -1183,7 +1202,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   // 4 * tile + r16 % 4 at the 8 positions that operand block kb covers (the
   // weight operand's order: bytes {0, 16, 8, 24}[kb] + 0..7 of each group)
   long aop[TILES][GS];
-  float pscale[TILES][4];  // 2^-s * 2^(-7 kb) of the lane's output rows
+  float pscale[TILES][4];  // 2^-s * 256^(3 - kb) of the lane's output rows
   {
     const int dt = r16 >> 2;
     const int base = ((kb & 1) << 4) | ((kb & 2) << 2);  // {0, 16, 8, 24}[kb]
@@ -1198,14 +1217,24 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
         aop[t][g] = *reinterpret_cast<const long*>(src);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pscale[t][i] = 4 * t + i < M ? ldexpf(ysc[4 * t + i < M ? 4 * t + i : 0], -7 * kb) : 0.f;
+      for (int i = 0; i < 4; ++i) pscale[t][i] = 4 * t + i < M ? ldexpf(ysc[4 * t + i < M ? 4 * t + i : 0], 8 * (3 - kb)) : 0.f;
     }
   }
 
-  // ---- main loop over row blocks
+  // ---- main loop over row blocks.  Two to four rows (one row block in
+  // flight): each part of a row block's buffer is refilled with row block
+  // j + D as soon as it has been read, so the wave's next loads go out while
+  // it computes; with the whole block issued after the compute the memory sat
+  // idle while every wave computed.  One row keeps two whole blocks in flight.
+  constexpr bool ROLL = M > 1;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const i32x4 izero = {0, 0, 0, 0};
-  auto compute = [&](const WB& b, int j) {
+  auto compute = [&](WB& b, int j) {
+    const int jn = j + D;
+    const int rln = jn * kRB + r16;
+    const bool mine = rln >= rlo && rln < rhi;
+    const uint32_t ro = mine ? (uint32_t)jn * (kRB * a.row_bytes) : kFarRows;
+    const uint32_t rod = mine ? (uint32_t)jn * a.d_tile_bytes : kFarRows;
     float Y[TILES][4];
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -1215,12 +1244,19 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
     for (int q = 0; q < GS / 2; ++q) {
       uint2 wq[2];
       pair_to_operands(b.q[q], wq[0], wq[1]);
+      // groups past the slice have zero operands; their scale is some other
+      // finite one, or zero past the plane
+      float dpair[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) dpair[h] = f16_bits_to_f32((b.d[q] >> (16 * h)) & 0xFFFFu);
+      if constexpr (ROLL) {
+        issue_codes<GS>(b, q, rq, qoff[q], ro);
+        if (DALIGN ? q % 4 == 3 : true) issue_scales<GS, DALIGN>(b, DALIGN ? q / 4 : q, rd, doff, gq, r16, rod);
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int g = 2 * q + h;
-        // groups past the slice have zero operands; their scale is some other
-        // finite one, or zero past the plane
-        const float dd = f16_bits_to_f32((b.d[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+        const float dd = dpair[h];
         const long bq = (long)(((uint64_t)wq[h].y << 32) | wq[h].x);
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
@@ -1243,8 +1279,8 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       const int j = j0 + i;
-      if (j < nrb) compute(wb[i], j);
-      issue(j + D, wb[i]);
+      if (j < nrb) compute(wb[i], j);  // (ROLL: its loads of row block j + D included)
+      if constexpr (!ROLL) issue(j + D, wb[i]);
       if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
         __syncthreads();
         reduce_round(wr, part, NW, RBR, M, 4, rb0, nrb, j / RBR, blockIdx.y);
