@@ -181,8 +181,8 @@ size_t kq_workspace_bytes(int32_t op, kq_format fmt, int64_t M, int64_t N,
  * product (measured: 7.7e-4 of the bound for an element 2^24 times the others
  * with no rotation; near 1e-6 of it with a 128-element rotation, which spreads
  * such elements over the block).  Q8_0 with M <= 4 holds each element to
- * 2^-27 of the largest |x'| of its row within the K slice (an output whose
- * weights touch only elements more than about 10^5 below that can miss the
+ * 2^-30 of the largest |x'| of its row within the K slice (an output whose
+ * weights touch only elements more than about 10^6 below that can miss the
  * bound); M >= 5: 2^-17 of itself.
  * split_k: 1 = one pass over K; S > 1 splits K into S contiguous ranges of
  * whole blocks whose fp32 partial sums are added in ascending order
