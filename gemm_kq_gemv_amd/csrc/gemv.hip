@@ -903,15 +903,19 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
 // and 2^-s are applied once per row block, and the four lane blocks' partials
 // are added by the LDS reduction in a fixed order.
 
-// 16 groups of 32 per wave (two chunks of scales).  Row blocks of weight loads
-// in flight: two for one activation row, one for two to four (their digit
-// operands take the registers), two again for the bf16 kernel of five to
-// eight rows, whose waves may use 256 VGPRs (at most 8 waves).
+// Groups of 32 per wave: 16 (two chunks of scales) up to four activation
+// rows; 8 for the bf16 kernel of five to eight rows, whose waves then fit 168
+// VGPRs, so that a workgroup holds 10 waves (two K slices at K=5120) instead
+// of 5 of 16 groups (M=8: 26.2 -> 22.8 us; its LDS, the staged rows of x,
+// leaves room for one workgroup per compute unit).  Row blocks of weight
+// loads in flight: two for one activation row, one for two to four (their
+// digit operands take the registers), two again for five to eight.
 __host__ __device__ constexpr int q8_rbr(int M) { return M == 1 ? 8 : 2; }  // row blocks per reduction round
-__host__ __device__ constexpr int q8_maxw(int M) { return M <= 4 ? 12 : 8; }
+__host__ __device__ constexpr int q8_maxw(int) { return 12; }
+__host__ __device__ constexpr int q8_gs(int M) { return M > 4 ? 8 : 16; }
 template <int M>
 struct Q8Cfg {
-  static constexpr int GS = 16;
+  static constexpr int GS = q8_gs(M);
   static constexpr int D = M == 1 || M > 4 ? 2 : 1;
   static constexpr int RBR = q8_rbr(M);
   static constexpr int MAXW = q8_maxw(M);
@@ -1637,7 +1641,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   const int n = block_len > 1 ? block_len : 1;
   // PQ2_0: half-word lanes unless a rotation block needs a whole wave
   const int epl = pq2 ? (n <= 512 ? 8 : 16) : 0;
-  const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : Q8Cfg<1>::GS;
+  const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : q8_gs((int)M);
   const int MAXW = pq2 ? (epl == 8 ? Pq2Cfg<8>::MAXW : Pq2Cfg<16>::MAXW) : q8_maxw((int)M);
   const int G = (int)(K / GROUP);
   const int U = n > GROUP ? n / GROUP : 1;
@@ -1934,8 +1938,12 @@ int launch_gemv_loads_twin(int fmt, const void* packed, int64_t N, int64_t K, co
     }
   } else {
     constexpr int GS = Q8Cfg<1>::GS;
-    if (Q8Cfg<1>::D == 2 && (M == 1 || M > 4)) {
-      static_assert(Q8Cfg<1>::D == 2 && Q8Cfg<8>::D == 2, "two row blocks in flight for 1 and 5..8 rows");
+    static_assert(Q8Cfg<1>::D == 2 && Q8Cfg<8>::D == 2, "two row blocks in flight for 1 and 5..8 rows");
+    if (M > 4) {
+      constexpr int GS8 = Q8Cfg<8>::GS;
+      if (p.dalign) hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS8, 2, true>), grid, block, 0, st, a, m, sink);
+      else hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS8, 2, false>), grid, block, 0, st, a, m, sink);
+    } else if (M == 1) {
       if (p.dalign) hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS, 2, true>), grid, block, 0, st, a, m, sink);
       else hipLaunchKernelGGL((gemv_loads_twin_kernel<false, GS, 2, false>), grid, block, 0, st, a, m, sink);
     } else {
