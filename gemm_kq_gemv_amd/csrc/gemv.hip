@@ -1097,7 +1097,13 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   for (int i = 0; i < DPRE; ++i) issue(i, wb[i]);
 
   // ---- prologue: stage x (.) s in LDS, butterflies with stride < 16 in
-  // registers, wider ones in LDS
+  // registers, wider ones in LDS.  Without LDS stages each thread's values
+  // are final in its registers, so their maxima are taken there (one LDS
+  // pass and one barrier fewer).
+  const bool reg_max = a.log2n <= 4;
+  float mx[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) mx[m] = 0.f;
   {
     const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
 #pragma unroll
@@ -1132,10 +1138,20 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx[m] = fmaxf(mx[m], fabsf(v[i]));  // (zeros past the slice)
     }
   }
+  if (reg_max) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float w = wave_max_nonneg(mx[m]);
+      if (lane == 0) rmax[m * NW + wave] = w;
+    }
+    if (tid < 4) reinterpret_cast<uint32_t*>(zeros)[tid] = 0u;
+  }
   __syncthreads();
-  if (a.log2n > 4) {
+  if (!reg_max) {
     lds_stages(xs, KRmax, KR, a.log2n, M);
     __syncthreads();
   }
@@ -1143,8 +1159,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   // ---- digits: the slice's largest |x'| per row, then every 8-element chunk
   // of x' rewritten in place as its four digit planes
   const int nch = KR >> 3;
-  {
-    float mx[M];
+  if (!reg_max) {
 #pragma unroll
     for (int m = 0; m < M; ++m) mx[m] = 0.f;
     for (int c = tid; c < nch; c += blockDim.x) {
@@ -1162,8 +1177,8 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
       if (lane == 0) rmax[m * NW + wave] = w;
     }
     if (tid < 4) reinterpret_cast<uint32_t*>(zeros)[tid] = 0u;
+    __syncthreads();
   }
-  __syncthreads();
   float cs[M];   // inv_sqrt_n * 2^s: x' 2^s = staged value * cs
   float ysc[M];  // 2^-s
 #pragma unroll
