@@ -431,8 +431,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the measured unit "
-              "is the single-GPU kernel at its real shape; DESIGN.md says how it would shard)",
-              file=sys.stderr)
+              "is the single-GPU kernel at its real shape)", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
