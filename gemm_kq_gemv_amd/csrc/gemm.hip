@@ -101,8 +101,9 @@ struct GemmArgs {
   float* part;          // S > 1: fp32 partials [S][M][N]
 };
 
-// 8 PQ2_0 codes (16 bits, code j at bits 2j) -> 8 bf16 values (q-1)*d, as 4
-// dwords in element order
+// 8 PQ2_0 codes (16 bits of a word in the block's own order, code j at bits
+// 2j, after pq2_load_word) -> 8 bf16 values (q-1)*d, as 4 dwords in element
+// order
 __device__ __forceinline__ uint4 dequant8_pq2(uint32_t h, float d) {
   const uint32_t e = h & 0x3333u;         // codes 0, 2, 4, 6 in nibbles 0..3
   const uint32_t o = (h >> 2) & 0x3333u;  // codes 1, 3, 5, 7
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::WPC) void gemm_kernel(GemmArgs a) {
     if (!unit_ok(i)) return;
     const float d = f16_bits_to_f32(rdd[i]);
     uint4 v;
-    if constexpr (PQ2) v = dequant8_pq2(rq[i] >> (16 * (kt & 1)), d);
+    if constexpr (PQ2) v = dequant8_pq2(pq2_load_word(rq[i]) >> (16 * (kt & 1)), d);
     else v = dequant8_q8(rq8[i], d);
     *reinterpret_cast<uint4*>(smem + stage * STAGE_BYTES + A_BYTES + w_lds + i * RPP * ROWB) = v;
   };

@@ -10,7 +10,7 @@
 // The product is bandwidth-bound, so the arithmetic has to stay well under
 // one vector instruction per weight.  The multiply-adds go to the matrix
 // cores and the vector ALUs only unpack:
-// * PQ2_0.  Three or four bit operations per 32-bit word turn 16 2-bit codes
+// * PQ2_0.  Three bit operations per stored 32-bit word turn 16 2-bit codes
 //   into 16 signed E2M1 (fp4) operands of value (c - 1) / 2, so that
 //   v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 weight rows x 128 codes
 //   (one quantization group) by a 16-row operand that holds x' as four e5m2
@@ -339,12 +339,13 @@ __device__ __forceinline__ void pair_to_operands(const uint4& v, uint2& g0, uint
   g1 = make_uint2(z, w);
 }
 
-// The 16 2-bit codes of one word (code j at bits 2j) as signed E2M1 (fp4)
-// operands of value (c - 1) / 2: code 0 -> -0.5 (1001), 1 -> -0 (1000),
-// 2 -> +0.5 (0001).  Code 3 is not a PQ2_0 value (the format maps only codes
-// 0, 1 and 2, and its packer never writes 3); it becomes +0 (0000).  Even
-// codes go to the nibbles of `ev`, odd ones to those of `od` (code 2i and
-// 2i+1 to nibble i).  Nibble bits: [3] = ~b1, [2] = [1] = 0, [0] = ~b0.
+// The 16 2-bit codes of one stored word (code j: b0 at bit 2j, b1 at bit
+// (2j + 3) mod 32, see pq2_store_word) as signed E2M1 (fp4) operands of value
+// (c - 1) / 2: code 0 -> -0.5 (1001), 1 -> -0 (1000), 2 -> +0.5 (0001).  Code
+// 3 is not a PQ2_0 value (the format maps only codes 0, 1 and 2, and its
+// packer never writes 3); it becomes +0 (0000).  Even codes go to the nibbles
+// of `ev`, odd ones to those of `od` (code 2i and 2i+1 to nibble i).  Nibble
+// bits: [3] = ~b1, [2] = [1] = 0, [0] = ~b0.
 // Signed operands keep every product of a zero weight at zero: the matrix
 // core sums the products of one instruction aligned to the largest of them,
 // so the smaller ones keep only about 2^-17 of it, and that must be measured
@@ -359,18 +360,14 @@ constexpr uint32_t bitop3_table(F f) {
   return t;
 }
 __device__ __forceinline__ void ternary_fp4(uint32_t w, uint32_t& ev, uint32_t& od) {
-  // p0..p3 are the bits of a nibble; M1 marks p0.  The second input carries
-  // b0 to p0, the third b1 to p3 with p1 and p2 forced to 1, so that its
-  // complement clears them.  Five instructions for 16 codes: one
-  // v_bitop3_b32 (any function of three inputs) per half, and the shifts and
-  // ors that line the bits up.
-  constexpr uint32_t M1 = 0x11111111u, P12 = 0x66666666u;
-  // m ? ~x : ~y  -- p0: ~b0; p1, p2: 0; p3: ~b1
-  constexpr uint32_t kSel = bitop3_table([](int m, int x, int y) { return m ? !x : !y; });
-  // even codes: b0 at p0, b1 at p1 (moved to p3)
-  ev = __builtin_amdgcn_bitop3_b32(M1, w, (w << 2) | P12, kSel);
-  // odd codes: b0 at p2 (moved to p0), b1 at p3
-  od = __builtin_amdgcn_bitop3_b32(M1, w >> 2, w | P12, kSel);
+  // The even codes' bits already sit at nibble bits 0 and 3, the odd codes'
+  // two places up: one v_bitop3_b32 (~x & m) per half, after a rotate
+  // (v_alignbit_b32) for the odd half.  Three instructions for 16 codes.
+  constexpr uint32_t M03 = 0x99999999u;
+  constexpr uint32_t kSel = bitop3_table([](int m, int x, int) { return m && !x; });
+  ev = __builtin_amdgcn_bitop3_b32(M03, w, w, kSel);
+  const uint32_t r = __builtin_amdgcn_alignbit(w, w, 2);  // w rotated down by two
+  od = __builtin_amdgcn_bitop3_b32(M03, r, r, kSel);
 }
 
 // start of part i when parts of `base` items get one more for i < rem

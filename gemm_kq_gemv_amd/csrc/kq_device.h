@@ -83,6 +83,22 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 __host__ __device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t wr, int64_t nb) {
   return (((n >> 4) * nb + (wr >> 3)) << 7) + ((n & 15) << 3) + (wr & 7);
 }
+// PQ2_0 code words in the code plane.  The block's word i (its code bytes
+// 4i..4i+3, little-endian) holds codes 16i + j at bits 2j (low bit b0) and
+// 2j + 1 (high bit b1).  The stored word keeps every b0 in place and rotates
+// the b1 bits up by two: b1 of code j sits at bit (2j + 3) mod 32.  Then
+// codes 2i have their bits at 4i and 4i + 3, codes 2i + 1 at 4i + 2 and
+// 4i + 5, exactly the sign and mantissa bits of fp4 nibble i once the word
+// (or, for the odd codes, the word rotated down by two) is complemented and
+// masked: two and three instructions for the GEMV's operands.
+__host__ __device__ __forceinline__ uint32_t pq2_store_word(uint32_t w) {
+  const uint32_t hi = w & 0xAAAAAAAAu;
+  return (w & 0x55555555u) | (hi << 2) | (hi >> 30);
+}
+__host__ __device__ __forceinline__ uint32_t pq2_load_word(uint32_t s) {
+  const uint32_t hi = s & 0xAAAAAAAAu;
+  return (s & 0x55555555u) | (hi >> 2) | (hi << 30);
+}
 // Scale plane tiling: the fp16 scale of block b of row n lives in chunk
 // (n / 16, b / 8) -- 16 rows x 8 blocks, row n % 16 at byte 16 * (n % 16),
 // block b % 8 at byte 2 * (b % 8) within it -- and chunk (t, c) starts at

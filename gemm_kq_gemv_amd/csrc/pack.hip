@@ -9,6 +9,8 @@
 // division is the IEEE one, and an all-zero group keeps d = 0 with the
 // neutral code (1 for PQ2_0, 0 for Q8_0).
 //
+// PQ2_0 words are stored with their high code bits rotated (pq2_store_word).
+//
 // Launch shape: one thread per 32-bit code word, in row-major order over the
 // rows padded to whole 16-row tiles.  For PQ2_0 a word holds 16 codes and 8
 // consecutive threads cover one 128-group; for Q8_0 a word holds 4 int8 and 8
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256) void pack_pq2_kernel(
     word |= (uint32_t)q << (2 * j);
   }
   if (in_plane) {
-    qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? word : 0u;
+    qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? pq2_store_word(word) : 0u;
     if ((g & 7) == 0) store_scale(dplane, g, words_per_row, C, live ? d16 : (uint16_t)0);
   }
 }
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void unpack_pq2_kernel(
     float* __restrict__ W, int64_t n_words, int64_t words_per_row, int64_t C) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_words) return;
-  uint32_t word = qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)];
+  uint32_t word = pq2_load_word(qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)]);
   float d = f16_bits_to_f32(dplane[tiled_scale(g / words_per_row, (g % words_per_row) >> 3, C)]);
   float4* dst = reinterpret_cast<float4*>(W) + g * 4;
 #pragma unroll
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void transcode_ptq1_kernel(
     const int n = e < 80 ? e / 16 : e < 120 ? (e - 80) / 8 : (e - 120) / 2;
     word |= ptq1_digit(byte_at(byte), n) << (2 * j);
   }
-  qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? word : 0u;
+  qs[tiled_word(g / words_per_row, g % words_per_row, words_per_row >> 3)] = live ? pq2_store_word(word) : 0u;
   if (i == 0)
     store_scale(dplane, g, words_per_row, C, live ? (uint16_t)(byte_at(26) | (byte_at(27) << 8)) : (uint16_t)0);
 }

@@ -37,11 +37,13 @@
  *                and starts at byte 512 * (t * nb + b); inside it, row
  *                n % 16 occupies bytes 32 * (n % 16) .. +31.  Rows past N
  *                in the last tile are zero.  Plane size:
- *                ceil(N/16) * 16 * nb * 32 bytes.  Inside a block the 32
- *                bytes are those of the GGUF-style block: for PQ2_0,
- *                reading 4 bytes as a little-endian u32 gives word i of the
- *                block holding element 16*i + j at bits 2*j ([BT] 3.1
- *                "Word view"); for Q8_0 they are the 32 int8 codes.
+ *                ceil(N/16) * 16 * nb * 32 bytes.  Inside a block: for
+ *                Q8_0 the 32 int8 codes in order; for PQ2_0, 8 little-endian
+ *                u32 words, word i holding the codes of elements 16*i + j
+ *                (j = 0..15) -- the block's word view ([BT] 3.1 "Word
+ *                view": code j at bits 2*j, 2*j + 1) with the high bit of
+ *                each code moved: bit 0 of code j at bit 2*j, bit 1 at bit
+ *                (2*j + 3) mod 32 (the odd bits rotated up by two).
  *     d plane  : at byte offset round_up(qs plane size, 256): one IEEE
  *                binary16 scale per block (little endian), in chunks of
  *                16 rows x 8 blocks: the scale of block b of row n sits in

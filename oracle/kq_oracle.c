@@ -191,7 +191,7 @@ int kqo_pack_q8_aos(const float *W, int64_t N, int64_t K, uint8_t *aos)
 }
 
 /* ======================================================================== */
-/* Layout change AoS -> planar (byte moves only).                           */
+/* Layout change AoS -> planar (byte moves; PQ2_0 code bits placed anew).    */
 /* ======================================================================== */
 
 static int fmt_group(int fmt) { return fmt == 1 ? 128 : (fmt == 2 ? 32 : 0); }
@@ -210,11 +210,28 @@ int64_t kqo_planar_bytes(int fmt, int64_t N, int64_t K)
 
 /* The 32 code bytes of block b of row n go to tile (n / 16, b): 16 rows x
  * 32 bytes, row n % 16 at byte 32 * (n % 16), tile (t, b) at byte
- * 512 * (t * nb + b).  Rows past N in the last tile stay zero.  The fp16
+ * 512 * (t * nb + b).  Rows past N in the last tile stay zero.  Q8_0 code
+ * bytes are copied as they are.  PQ2_0 code word i of a block (its bytes
+ * 4i..4i+3, little-endian) holds the same 16 codes as the block's word i
+ * [BT 3.1 word view], with code j's low bit at bit 2j as there and its high
+ * bit at bit (2j + 3) mod 32 instead of 2j + 1 (pq2_place_codes).  The fp16
  * scales follow at the first 256-byte boundary, in chunks of 16 rows x 8
  * blocks: the scale of block b of row n sits in chunk (n / 16, b / 8), which
  * starts at 256 * ((n / 16) * ceil(nb / 8) + b / 8), at byte
  * 16 * (n % 16) + 2 * (b % 8) of it.  Slots past N or nb stay zero. */
+/* One PQ2_0 code word of the planar layout from the block's word view:
+ * code j (bits 2j, 2j+1 of `word`) -> low bit at 2j, high bit at (2j+3) % 32. */
+static uint32_t pq2_place_codes(uint32_t word)
+{
+    uint32_t out = 0;
+    for (int j = 0; j < 16; ++j) {
+        uint32_t q = (word >> (2 * j)) & 3u;
+        out |= (q & 1u) << (2 * j);
+        out |= (q >> 1) << ((2 * j + 3) % 32);
+    }
+    return out;
+}
+
 int kqo_aos_to_planar(int fmt, const uint8_t *aos, int64_t N, int64_t K,
                       uint8_t *planar)
 {
@@ -229,7 +246,17 @@ int kqo_aos_to_planar(int fmt, const uint8_t *aos, int64_t N, int64_t K,
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < nb; ++b) {
             const uint8_t *blk = aos + (n * nb + b) * 34;
-            memcpy(planar + ((n / 16) * nb + b) * 512 + (n % 16) * 32, blk + 2, 32);
+            uint8_t *dst = planar + ((n / 16) * nb + b) * 512 + (n % 16) * 32;
+            memcpy(dst, blk + 2, 32);
+            if (fmt == 1) {
+                for (int i = 0; i < 8; ++i) {
+                    const uint8_t *p = blk + 2 + 4 * i;
+                    uint32_t w = (uint32_t)p[0] | ((uint32_t)p[1] << 8) |
+                                 ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+                    uint32_t v = pq2_place_codes(w);
+                    for (int k = 0; k < 4; ++k) dst[4 * i + k] = (uint8_t)(v >> (8 * k));
+                }
+            }
             int64_t at = d_off + ((n / 16) * chunks + b / 8) * 256 + (n % 16) * 16 + (b % 8) * 2;
             planar[at + 0] = blk[0];
             planar[at + 1] = blk[1];

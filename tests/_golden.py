@@ -39,15 +39,33 @@ def sparse_block(s: str, length: int) -> np.ndarray:
     return w
 
 
-def code_rows(plane, N: int, K: int, fmt: int):
-    """Row-major code bytes [N][32 * blocks] from a packed buffer: the code
-    plane holds tiles of 16 rows x 32 bytes (one block), row r of a tile at
-    byte 32 r, tiles ordered by 16-row block and then by block along K."""
-    import numpy as np
+def stored_code_rows(plane, N: int, K: int, fmt: int):
+    """Row-major code bytes [N][32 * blocks] as stored in a packed buffer: the
+    code plane holds tiles of 16 rows x 32 bytes (one block), row r of a tile
+    at byte 32 r, tiles ordered by 16-row block and then by block along K."""
     nb = K // (128 if fmt == 1 else 32)
     nt = (N + 15) // 16
     tiles = np.asarray(plane)[:nt * nb * 512].reshape(nt, nb, 16, 32)
     return tiles.transpose(0, 2, 1, 3).reshape(nt * 16, nb * 32)[:N]
+
+
+def pq2_word_view(stored):
+    """Stored PQ2_0 code bytes -> the block's own qs bytes (GGUF word view,
+    code j of a little-endian word at bits 2j, 2j + 1).  A stored word keeps
+    the even bits (the codes' low bits) in place and holds the odd bits (the
+    high bits) rotated up by two, so they rotate back down by two."""
+    s = np.ascontiguousarray(stored, dtype=np.uint8)
+    w = s.view("<u4").astype(np.uint64)
+    hi = w & 0xAAAAAAAA
+    back = (w & 0x55555555) | (hi >> 2) | ((hi << 30) & 0xFFFFFFFF)
+    return back.astype("<u4").view(np.uint8).reshape(s.shape)
+
+
+def code_rows(plane, N: int, K: int, fmt: int):
+    """Row-major code bytes [N][32 * blocks] of a packed buffer in the
+    blocks' own byte order (PQ2_0 words back in the GGUF word view)."""
+    rows = stored_code_rows(plane, N, K, fmt)
+    return pq2_word_view(rows) if fmt == 1 else rows
 
 
 def d_offset(N: int, K: int, fmt: int) -> int:

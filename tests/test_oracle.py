@@ -166,17 +166,25 @@ def test_pq2_aos_to_planar_layout():
     # block b at 2 b; slots past N or past the 2 blocks zero
     assert pl.size == d_off + 256
     tiles = pl[:qs_bytes].reshape(2, 16, 32)
+    # stored word i of a block holds its elements 16i + j: the code's low bit
+    # at bit 2j, its high bit at bit (2j + 3) mod 32
     for n in range(N):
         for b in range(2):
-            assert np.array_equal(tiles[b, n], aos[n, b, 2:])
+            words = tiles[b, n].copy().view("<u4")
+            for e in range(128):
+                q = (int(aos[n, b, 2 + e // 4]) >> (2 * (e % 4))) & 3
+                w, j = int(words[e // 16]), e % 16
+                assert (w >> (2 * j)) & 1 == q & 1, (n, b, e)
+                assert (w >> ((2 * j + 3) % 32)) & 1 == q >> 1, (n, b, e)
     assert not tiles[:, N:].any()
     chunk = pl[d_off:].reshape(16, 8, 2)
     assert np.array_equal(chunk[:N, :2], aos[:, :, :2])
     assert not chunk[N:].any() and not chunk[:, 2:].any()
-    # word view of a row's code bytes: element 16i + j at bits 2j of LE word i
+    # decoding the stored words by that rule gives the oracle's dequantization
     row_codes = np.ascontiguousarray(tiles[:, :N].transpose(1, 0, 2)).reshape(N, K // 4)
-    words = row_codes.view("<u4").reshape(N, K // 16)
-    codes = np.stack([(words >> (2 * j)) & 3 for j in range(16)], axis=-1).reshape(N, K)
+    words = row_codes.view("<u4").reshape(N, K // 16).astype(np.int64)
+    codes = np.stack([((words >> (2 * j)) & 1) | (((words >> ((2 * j + 3) % 32)) & 1) << 1)
+                      for j in range(16)], axis=-1).reshape(N, K)
     dF = np.ascontiguousarray(chunk[:N, :2]).view("<f2").astype(np.float64).reshape(N, K // 128)
     deq = (codes.astype(np.float64) - 1) * np.repeat(dF, 128, axis=1)
     assert np.array_equal(deq, oracle.unpack_pq2_aos(aos.reshape(-1), N, K))
@@ -209,7 +217,8 @@ def test_aos_to_planar_multi_tile_multi_chunk(fmt, N, K):
         for b in range(nb):
             t = n // 16
             q0 = 512 * (t * nb + b) + 32 * (n % 16)
-            assert np.array_equal(pl[q0:q0 + 32], aos[n, b, 2:]), (n, b)
+            got = G.pq2_word_view(pl[q0:q0 + 32]) if fmt == 1 else pl[q0:q0 + 32]
+            assert np.array_equal(got, aos[n, b, 2:]), (n, b)
             d0 = d_off + 256 * (t * C + b // 8) + 16 * (n % 16) + 2 * (b % 8)
             assert np.array_equal(pl[d0:d0 + 2], aos[n, b, :2]), (n, b)
     # everything else (code rows past N, scale slots past N or nb, the gap
