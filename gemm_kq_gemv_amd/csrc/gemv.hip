@@ -66,6 +66,7 @@ constexpr uint32_t kFarRows = 0x40000000u;
 constexpr int64_t kMaxWgBytes = int64_t(1) << 29;
 constexpr int kLdsBudget = 160 * 1024;
 constexpr int kTargetWGs = 256;  // one workgroup per CU
+constexpr int kEarlyWave = 8;
 
 // One weight set of a multi-set call: its planes, output and row blocks, and
 // the first workgroup of the grid that works on it.
@@ -157,6 +158,46 @@ __device__ __forceinline__ WgRows wg_rows(const GemvArgs& a) {
   w.r0 = a.row_unit * part_start(bx, base, rem);
   const int64_t e = (int64_t)a.row_unit * part_start(bx + 1, base, rem);
   w.r1 = (int)(e < w.N ? e : w.N);
+  w.rb0 = w.r0 / kRB;
+  w.rb1 = (w.r1 + kRB - 1) / kRB;
+  return w;
+}
+
+// The arguments a wave needs before its first loads, passed as the kernel's
+// leading scalar parameters: the first 14 dwords of a kernel's arguments are
+// preloaded into scalar registers before its waves start, so the activation
+// and weight loads go out without waiting for a scalar load of the argument
+// block.  The rest stays in GemvArgs (loaded behind the first vector loads).
+struct GemvHead {
+  const uint8_t* qs;
+  const uint8_t* dpl;
+  const float* x;
+  const int8_t* signs;
+  int q_base, q_rem;  // 16-row blocks per workgroup (one weight set)
+  int n;              // rows (fits 32 bits)
+  int G;              // groups per row: 32 G code bytes a row, 256 ceil(G/8) scale bytes a tile
+  int u_br;           // K slices of whole rotation blocks: u_base | u_rem << 16
+  int U;              // groups per rotation block
+};
+#define KQ_HEAD_PARAMS                                                                        \
+  const uint8_t *__restrict__ h_qs, const uint8_t *__restrict__ h_dpl,                       \
+      const float *__restrict__ h_x, const int8_t *__restrict__ h_sg, int h_qb, int h_qr,    \
+      int h_n, int h_g, int h_ubr, int h_u
+#define KQ_HEAD_MAKE {h_qs, h_dpl, h_x, h_sg, h_qb, h_qr, h_n, h_g, h_ubr, h_u}
+#define KQ_HEAD_ARGS(h)                                                                       \
+  (h).qs, (h).dpl, (h).x, (h).signs, (h).q_base, (h).q_rem, (h).n, (h).G, (h).u_br, (h).U
+static_assert(sizeof(GemvHead) == 56, "the head is 14 preloaded dwords");
+
+__device__ __forceinline__ WgRows wg_rows_head(const GemvHead& h) {
+  const int b = (int)blockIdx.x;
+  WgRows w;
+  w.qs = h.qs;
+  w.dpl = h.dpl;
+  w.out = nullptr;
+  w.N = h.n;
+  w.r0 = kRB * part_start(b, h.q_base, h.q_rem);
+  const int e = kRB * part_start(b + 1, h.q_base, h.q_rem);
+  w.r1 = e < h.n ? e : h.n;
   w.rb0 = w.r0 / kRB;
   w.rb1 = (w.r1 + kRB - 1) / kRB;
   return w;
@@ -398,6 +439,36 @@ __device__ __forceinline__ void reduce_round(const WgRows& a, const float* part,
   }
 }
 
+// One activation row: each wave leaves one partial per output row (its four
+// lane blocks already added), [RBR][16 rows][NWP wave slots]; the NW of them
+// are added as a fixed tree, read as NWP / 4 16-byte words.
+template <int NWP>
+__device__ __forceinline__ void reduce_round_one(const WgRows& a, const float* part, int NW, int RBR,
+                                                 int rb0, int nrb, int round, int s) {
+  const float* pr = part + (round & 1) * RBR * kRB * NWP;
+  for (int it = threadIdx.x; it < RBR * kRB; it += blockDim.x) {
+    const int jr = it / kRB, r = it % kRB;
+    const int j = round * RBR + jr;
+    const int row = (rb0 + j) * kRB + r;
+    if (j < nrb && row >= a.r0 && row < a.r1) {
+      const float4* p = reinterpret_cast<const float4*>(pr + it * NWP);
+      float v[NWP];
+#pragma unroll
+      for (int q = 0; q < NWP / 4; ++q) {
+        const float4 f = p[q];
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+#pragma unroll
+      for (int w = 0; w < NWP; ++w) v[w] = w < NW ? v[w] : 0.f;
+#pragma unroll
+      for (int h = 1; h < NWP; h *= 2)
+#pragma unroll
+        for (int w = 0; w + h < NWP; w += 2 * h) v[w] += v[w + h];
+      a.out[(int64_t)s * a.N + row] = v[0];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Weight loads of one row block for one wave (shared by every GEMV kernel and
 // by its loads-only twin): the codes of the wave's GS groups, one 16-byte
@@ -492,8 +563,11 @@ struct Pq2Cfg {
 // blocks hold one term each), else 1.
 __host__ __device__ inline int pq2_ks(int M) { return M == 1 ? 4 : 1; }
 __host__ __device__ inline int pq2_lds_part_offset(int M, int NW, int GS) { return NW * GS * M * 512; }
+// waves' slots per output row in the one-row partials (a multiple of four)
+__host__ __device__ constexpr int pq2_nwp(int GS) { return GS == 4 ? 12 : 8; }
 __host__ __device__ inline int pq2_lds_zero_offset(int M, int NW, int GS) {
-  return pq2_lds_part_offset(M, NW, GS) + 2 * NW * 8 * M * pq2_ks(M) * kRB * 4;
+  return pq2_lds_part_offset(M, NW, GS) +
+         (M == 1 ? 2 * 8 * kRB * pq2_nwp(GS) * 4 : 2 * NW * 8 * M * pq2_ks(M) * kRB * 4);
 }
 __host__ __device__ inline int pq2_lds_bytes(int M, int NW, int GS) { return pq2_lds_zero_offset(M, NW, GS) + 32; }
 
@@ -560,7 +634,8 @@ __device__ __forceinline__ float group_max(float v) {
 // separate instance: with the loop in the same function the compiler's
 // memory waits before the first row block covered nearly every later load.
 template <int M, bool DALIGN, int EPL, bool MULTI, bool FEW>
-__global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvArgs a) {
+__global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(KQ_HEAD_PARAMS, GemvArgs a) {
+  const GemvHead h = KQ_HEAD_MAKE;
   using C = Pq2Cfg<EPL>;
   constexpr int GS = C::GS, D = C::D, RBR = C::RBR, LPG = C::LPG;
   constexpr int TILES = (M + 3) / 4;
@@ -571,6 +646,8 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   // rows: operand row 4*m + t, every accumulator used, scales applied after.
   constexpr bool ONE = M == 1;
   constexpr int KS = ONE ? 4 : 1;
+  constexpr int NWP = pq2_nwp(GS);
+  static_assert(NWP >= C::MAXW && NWP % 4 == 0, "a slot for every wave");
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -579,15 +656,27 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   const int r16 = lane & 15, kb = lane >> 4;
 
   int g0, g1;
-  slice_groups(a, blockIdx.y, g0, g1);
+  {
+    const int ub = h.u_br & 0xFFFF, ur = h.u_br >> 16;
+    g0 = part_start(blockIdx.y, ub, ur) * h.U;
+    g1 = part_start(blockIdx.y + 1, ub, ur) * h.U;
+  }
+  const uint32_t row_bytes = 32u * (uint32_t)h.G, d_tile_bytes = 256u * (uint32_t)((h.G + 7) >> 3);
   const int gw = g0 + wave * GS;                // first group of this wave
   const int vg = min(max(g1 - gw, 0), GS);      // its real groups
   const int64_t kw0 = (int64_t)gw * 128;        // first element of its K-range
   uint8_t* areg = lds + wave * (GS * M * 512);  // its operand bytes
   float* part = reinterpret_cast<float*>(lds + pq2_lds_part_offset(M, NW, GS));
 
-  const WgRows wr = wg_rows<MULTI>(a);
-  args_in_one_batch(a, wr);
+  WgRows wr;
+  if constexpr (MULTI) {
+    wr = wg_rows<true>(a);
+    args_in_one_batch(a, wr);
+  } else {
+    wr = wg_rows_head(h);
+    wr.out = a.out;
+    wr.N = a.N;
+  }
   const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
@@ -597,7 +686,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   const bool live = lane / LPG < vg;
   auto load_x = [&](int m, float (&v)[EPL]) {
     if (live) {
-      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + kw0) + (EPL / 4) * lane;
+      const float4* src = reinterpret_cast<const float4*>(h.x + (int64_t)m * a.K + kw0) + (EPL / 4) * lane;
 #pragma unroll
       for (int i = 0; i < EPL / 4; ++i) {
         const float4 f = src[i];
@@ -611,16 +700,17 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   float xv[MPRE][EPL];
 #pragma unroll
   for (int m = 0; m < MPRE; ++m) load_x(m, xv[m]);
-  const bool has_signs = a.signs != nullptr;
+
+  const bool has_signs = h.signs != nullptr;
   uint32_t sw[EPL / 4];
 #pragma unroll
   for (int i = 0; i < EPL / 4; ++i) sw[i] = 0u;
   if (live && has_signs) {
     if constexpr (EPL == 8) {
-      const uint2 t = *reinterpret_cast<const uint2*>(a.signs + kw0 + 8 * lane);
+      const uint2 t = *reinterpret_cast<const uint2*>(h.signs + kw0 + 8 * lane);
       sw[0] = t.x; sw[1] = t.y;
     } else {
-      const uint4 t = *reinterpret_cast<const uint4*>(a.signs + kw0 + 16 * lane);
+      const uint4 t = *reinterpret_cast<const uint4*>(h.signs + kw0 + 16 * lane);
       sw[0] = t.x; sw[1] = t.y; sw[2] = t.z; sw[3] = t.w;
     }
   }
@@ -637,25 +727,32 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   using WB = WBuf<GS>;
   const int64_t wrow0 = (int64_t)rb0 * kRB;
   // codes: the workgroup's whole 16-row tiles (rows past N are zero padding)
-  const BufRsrc rq = make_rsrc(wr.qs + wrow0 * a.row_bytes, (uint32_t)nrb * kRB * a.row_bytes);
+  const BufRsrc rq = make_rsrc(wr.qs + wrow0 * row_bytes, (uint32_t)nrb * kRB * row_bytes);
   // scales: the workgroup's whole 16-row tiles of the scale plane (padding is zero)
-  const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * a.d_tile_bytes, (uint32_t)nrb * a.d_tile_bytes);
+  const BufRsrc rd = make_rsrc(wr.dpl + (int64_t)rb0 * d_tile_bytes, (uint32_t)nrb * d_tile_bytes);
   // this lane's row of block j, relative to the first block: inside the
   // workgroup's rows or loaded at kFarRows (zeros, no memory touched)
   const int rlo = wr.r0 - rb0 * kRB, rhi = wr.r1 - rb0 * kRB;
   auto issue = [&](int j, WB& b) {
     const int rl = j * kRB + r16;
     const bool mine = rl >= rlo && rl < rhi;
-    const uint32_t ro = mine ? (uint32_t)j * (kRB * a.row_bytes) : kFarRows;
-    const uint32_t rod = mine ? (uint32_t)j * a.d_tile_bytes : kFarRows;
+    const uint32_t ro = mine ? (uint32_t)j * (kRB * row_bytes) : kFarRows;
+    const uint32_t rod = mine ? (uint32_t)j * d_tile_bytes : kFarRows;
     issue_row_block<GS, DALIGN>(b, rq, rd, qoff, doff, gw, r16, ro, rod);
   };
   // Only the first row block is loaded before the prologue.  A wave stalls at a
   // load it cannot issue while the compute unit's memory pipeline is full, and
   // a stalled wave does no arithmetic; with all D blocks issued here the waves
   // sat through the fetch and rotated x only afterwards.
+  auto run = [&](auto early_tag) {
+  // EARLY: all D row blocks before the prologue (see kEarlyWave)
+  constexpr bool EARLY = decltype(early_tag)::value;
   WB wb[D];
   issue(0, wb[0]);
+  if constexpr (EARLY) {
+#pragma unroll
+    for (int i = 1; i < D; ++i) issue(i, wb[i]);
+  }
 
   // ---- per-wave prologue: rotation, per-group range scale, e5m2 terms
   float gsc[TILES][GS];  // 2^-e of (activation row 4*tile + kb, group)
@@ -755,8 +852,10 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
   }
   // the other row blocks in flight (kept here by the scheduling barriers)
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!EARLY) {
 #pragma unroll
-  for (int i = 1; i < D; ++i) issue(i, wb[i]);
+    for (int i = 1; i < D; ++i) issue(i, wb[i]);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // Lanes of rows past M and of groups past the slice read 32 zero bytes
   // (every wave stores the same zeros).  The operand bytes were written by
@@ -847,17 +946,25 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
           }
         }
     }
-    float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * KS * kRB;
     if constexpr (ONE) {
-      // lane block kb: term kb
-      pw[kb * kRB + r16] = 2.f * Y[0][0];
+      // lane block kb holds term kb: the four added across the wave
+      // ((kb 0 + kb 2) + (kb 1 + kb 3), the same bits in every lane of a row)
+      float t = Y[0][0];
+      t += xor_lane<32>(t);
+      t += xor_lane<16>(t);
+      if (kb == 0) part[((((j / RBR) & 1) * RBR + j % RBR) * kRB + r16) * NWP + wave] = 2.f * t;
     } else {
+      float* pw = part + ((((j / RBR) & 1) * NW + wave) * RBR + j % RBR) * M * KS * kRB;
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         const int mo = 4 * t + kb;
         if (mo < M) pw[mo * kRB + r16] = 2.f * ((Y[t][0] + Y[t][1]) + (Y[t][2] + Y[t][3]));
       }
     }
+  };
+  auto reduce = [&](int round) {
+    if constexpr (ONE) reduce_round_one<NWP>(wr, part, NW, RBR, rb0, nrb, round, blockIdx.y);
+    else reduce_round(wr, part, NW, RBR, M, KS, rb0, nrb, round, blockIdx.y);
   };
 
   if constexpr (FEW) {
@@ -866,7 +973,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
     for (int i = 0; i < D; ++i)
       if (i < nrb) compute(wb[i], i);
     __syncthreads();
-    reduce_round(wr, part, NW, RBR, M, KS, rb0, nrb, 0, blockIdx.y);
+    reduce(0);
     return;
   }
   for (int j0 = 0; j0 < nrb; j0 += D) {
@@ -877,11 +984,19 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(GemvAr
       issue(j + D, wb[i]);
       if (j < nrb && (j % RBR == RBR - 1 || j == nrb - 1)) {
         __syncthreads();
-        reduce_round(wr, part, NW, RBR, M, KS, rb0, nrb, j / RBR, blockIdx.y);
+        reduce(j / RBR);
       }
     }
   }
+  };
+  if constexpr (FEW) {
+    if (wave >= kEarlyWave) run(std::true_type{});
+    else run(std::false_type{});
+  } else {
+    run(std::false_type{});
+  }
 }
+
 
 // ---------------------------------------------------------------------------
 // Q8_0
@@ -1656,6 +1771,8 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, int block_len, int 
   const int GS = pq2 ? (epl == 8 ? Pq2Cfg<8>::GS : Pq2Cfg<16>::GS) : q8_gs((int)M);
   const int MAXW = pq2 ? (epl == 8 ? Pq2Cfg<8>::MAXW : Pq2Cfg<16>::MAXW) : q8_maxw((int)M);
   const int G = (int)(K / GROUP);
+  // the PQ2_0 kernels take the slice bounds as two 16-bit halves
+  if (pq2 && G >= 65536) return p;
   const int U = n > GROUP ? n / GROUP : 1;
   const int NU = G / U;
   auto waves_for = [&](int S) {
@@ -1749,11 +1866,39 @@ static int launch_kernel(Kernel k, const GemvArgs& a, const GemvPlan& p, hipStre
   return 0;
 }
 
+// the head of a launch: set 0's planes and rows (several sets read theirs
+// from the argument block)
+static GemvHead head_of(const GemvArgs& a) {
+  GemvHead h;
+  h.qs = a.nsets > 1 ? a.set[0].qs : a.qs;
+  h.dpl = a.nsets > 1 ? a.set[0].dpl : a.dpl;
+  h.x = a.x;
+  h.signs = a.signs;
+  h.q_base = a.q_base;
+  h.q_rem = a.q_rem;
+  h.n = (int)a.N;
+  h.G = a.G;
+  h.u_br = a.u_base | a.u_rem << 16;
+  h.U = a.U;
+  return h;
+}
+
+template <typename Kernel>
+static int launch_kernel_head(Kernel k, const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  if (p.lds_bytes > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+          hipSuccess)
+    return -1;
+  const GemvHead h = head_of(a);
+  hipLaunchKernelGGL(k, dim3(p.grid_x, p.split), dim3(p.nw * 64), p.lds_bytes, st, KQ_HEAD_ARGS(h), a);
+  return 0;
+}
+
 template <int M, int EPL, bool FEW>
 static int launch_pq2(const GemvArgs& a, const GemvPlan& p, bool multi, hipStream_t st) {
-  return multi ? launch_kernel(gemv_pq2_kernel<M, true, EPL, true, FEW>, a, p, st)
-         : p.dalign ? launch_kernel(gemv_pq2_kernel<M, true, EPL, false, FEW>, a, p, st)
-                    : launch_kernel(gemv_pq2_kernel<M, false, EPL, false, FEW>, a, p, st);
+  return multi ? launch_kernel_head(gemv_pq2_kernel<M, true, EPL, true, FEW>, a, p, st)
+         : p.dalign ? launch_kernel_head(gemv_pq2_kernel<M, true, EPL, false, FEW>, a, p, st)
+                    : launch_kernel_head(gemv_pq2_kernel<M, false, EPL, false, FEW>, a, p, st);
 }
 
 template <int M>
