@@ -2000,7 +2000,7 @@ int launch_gemv_multi(int fmt, int nsets, const void* const* packed, const int64
   int wgs[kMaxSets];
   const int grid = multi_split(fmt, nsets, N, K, M, block_len, p, wgs);
   if (grid < 1) return -2;
-  GemvArgs a;
+  GemvArgs a{};
   common_args(a, fmt, p, K, x, block_len, signs);
   a.nsets = nsets;
   int wg0 = 0;
@@ -2044,7 +2044,7 @@ int launch_gemv(int fmt, const void* packed, int64_t N, int64_t K, const float* 
   GemvPlan p = plan_gemv(fmt, M, N, K, block_len, split_req);
   if (p.split < 1) return -2;
   PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
-  GemvArgs a;
+  GemvArgs a{};
   common_args(a, fmt, p, K, x, block_len, signs);
   a.qs = pv.qs;
   a.dpl = pv.d;
@@ -2071,7 +2071,7 @@ int launch_gemv_loads_twin(int fmt, const void* packed, int64_t N, int64_t K, co
   GemvPlan p = plan_gemv(fmt, M, N, K, block_len, split_req);
   if (p.split < 1) return -2;
   PlanarView pv = planar_view(fmt, N, K, const_cast<void*>(packed));
-  GemvArgs a;
+  GemvArgs a{};
   common_args(a, fmt, p, K, x, block_len, nullptr);
   a.qs = pv.qs;
   a.dpl = pv.d;
