@@ -1150,14 +1150,21 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   const int rb0 = wr.rb0, rb1 = wr.rb1;
   const int nrb = rb1 - rb0;
 
-  // ---- activation loads first (rows past the first four after the weight
-  // loads, to bound the registers held)
-  constexpr int MPRE = M < 4 ? M : 4;
-  const int U16 = KR >> 4;  // 16-element units per activation row (<= threads)
-  const bool has_unit = tid < U16;
+  // ---- activation loads first.  A thread holds one 16-element unit of up to
+  // MR rows: for two to four rows the threads of units [0, U16) take the
+  // first MR rows and those of [U16, 2 U16) the rest (a slice has at most
+  // half as many units as the workgroup has threads), so every thread works
+  // on the prologue and none holds more than two rows.
+  constexpr int RG = M >= 2 ? 2 : 1;      // row groups
+  constexpr int MR = (M + RG - 1) / RG;   // rows per thread
+  const int U16 = KR >> 4;                // 16-element units per activation row
+  const int rg = tid >= U16 ? 1 : 0;
+  const int u = tid - rg * U16;           // the thread's unit
+  const bool has_unit = tid < RG * U16;
+  auto row_of = [&](int i) { return rg * MR + i; };
   auto load_row = [&](int m, float (&v)[16]) {
-    if (has_unit) {
-      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + k0) + 4 * tid;
+    if (has_unit && m < M) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K + k0) + 4 * u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 f = src[i];
@@ -1168,11 +1175,11 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
       for (int i = 0; i < 16; ++i) v[i] = 0.f;
     }
   };
-  float xv[MPRE][16];
+  float xv[MR][16];
   uint4 sg = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-  for (int m = 0; m < MPRE; ++m) load_row(m, xv[m]);
-  if (has_unit && a.signs) sg = *reinterpret_cast<const uint4*>(a.signs + k0 + 16 * tid);
+  for (int i = 0; i < MR; ++i) load_row(row_of(i), xv[i]);
+  if (has_unit && a.signs) sg = *reinterpret_cast<const uint4*>(a.signs + k0 + 16 * u);
 
   // ---- weight loads (pair q: groups 2q, 2q+1 of the wave)
   uint32_t qoff[GS / 2];
@@ -1216,17 +1223,15 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   float mx[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) mx[m] = 0.f;
+  float xr[MR][16];  // the thread's rows of x (.) s after the in-register stages
   {
     const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
+    for (int ir = 0; ir < MR; ++ir) {
+      const int m = row_of(ir);
       float v[16];
-      if (m < MPRE) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = xv[m < MPRE ? m : 0][i];
-      } else {
-        load_row(m, v);
-      }
+      for (int i = 0; i < 16; ++i) v[i] = xv[ir][i];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const uint32_t neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;  // int8 sign bit
@@ -1245,13 +1250,21 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
             }
         }
       }
-      if (has_unit) {
-        float4* dst = reinterpret_cast<float4*>(xs + m * KRmax) + 4 * tid;
+      // staged in LDS only for the rotation stages there (wider blocks);
+      // otherwise the digits are made from these registers
+      if (!reg_max && has_unit && m < M) {
+        float4* dst = reinterpret_cast<float4*>(xs + m * KRmax) + 4 * u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
       }
+      float vm = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx[m] = fmaxf(mx[m], fabsf(v[i]));  // (zeros past the slice)
+      for (int i = 0; i < 16; ++i) vm = fmaxf(vm, fabsf(v[i]));  // (zeros past the slice)
+#pragma unroll
+      for (int mm = 0; mm < M; ++mm)
+        if (mm == m) mx[mm] = vm;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xr[ir][i] = v[i];
     }
   }
   if (reg_max) {
@@ -1303,21 +1316,49 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   }
   {
     constexpr uint32_t kBias = 0x80808080u;
-    for (int c = tid; c < nch; c += blockDim.x) {
+    // one 8-element chunk of row m: its four digit planes at ptr
+    auto digits = [&](const float (&v)[8], float c, float4* ptr) {
+      uint32_t J[8];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float4* ptr = reinterpret_cast<float4*>(xs + m * KRmax + 8 * c);
-        const float4 f0 = ptr[0], f1 = ptr[1];
-        const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-        uint32_t J[8];
+      for (int i = 0; i < 8; ++i) J[i] = (uint32_t)(int)__builtin_rintf(v[i] * c) + kBias;
+      // plane t (digit t) is byte 3 - t of each J, top bit flipped
+      uint32_t lo[4], hi[4];
+      transpose_bytes(J[0], J[1], J[2], J[3], lo);
+      transpose_bytes(J[4], J[5], J[6], J[7], hi);
+      ptr[0] = __builtin_bit_cast(float4, make_uint4(lo[3] ^ kBias, hi[3] ^ kBias, lo[2] ^ kBias, hi[2] ^ kBias));
+      ptr[1] = __builtin_bit_cast(float4, make_uint4(lo[1] ^ kBias, hi[1] ^ kBias, lo[0] ^ kBias, hi[0] ^ kBias));
+    };
+    if (reg_max) {
+      // from the thread's registers: its unit's two chunks of each of its rows
+      if (has_unit) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) J[i] = (uint32_t)(int)__builtin_rintf(v[i] * cs[m]) + kBias;
-        // plane t (digit t) is byte 3 - t of each J, top bit flipped
-        uint32_t lo[4], hi[4];
-        transpose_bytes(J[0], J[1], J[2], J[3], lo);
-        transpose_bytes(J[4], J[5], J[6], J[7], hi);
-        ptr[0] = __builtin_bit_cast(float4, make_uint4(lo[3] ^ kBias, hi[3] ^ kBias, lo[2] ^ kBias, hi[2] ^ kBias));
-        ptr[1] = __builtin_bit_cast(float4, make_uint4(lo[1] ^ kBias, hi[1] ^ kBias, lo[0] ^ kBias, hi[0] ^ kBias));
+        for (int ir = 0; ir < MR; ++ir) {
+          const int m = row_of(ir);
+          float c = 0.f;
+#pragma unroll
+          for (int mm = 0; mm < M; ++mm)
+            if (mm == m) c = cs[mm];
+          if (m < M) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float v[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) v[i] = xr[ir][8 * h + i];
+              digits(v, c, reinterpret_cast<float4*>(xs + m * KRmax + 16 * u + 8 * h));
+            }
+          }
+        }
+      }
+    } else {
+      // in place, from the staged and rotated rows
+      for (int c = tid; c < nch; c += blockDim.x) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float4* ptr = reinterpret_cast<float4*>(xs + m * KRmax + 8 * c);
+          const float4 f0 = ptr[0], f1 = ptr[1];
+          const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+          digits(v, cs[m], ptr);
+        }
       }
     }
   }
