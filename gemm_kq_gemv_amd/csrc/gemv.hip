@@ -1157,6 +1157,7 @@ __global__ __launch_bounds__(Q8Cfg<M>::MAXW * 64) void gemv_q8_kernel(GemvArgs a
   // on the prologue and none holds more than two rows.
   constexpr int RG = M >= 2 ? 2 : 1;      // row groups
   constexpr int MR = (M + RG - 1) / RG;   // rows per thread
+  static_assert(GS * 32 / 16 * RG <= 64, "a wave's units of all row groups fit its lanes");
   const int U16 = KR >> 4;                // 16-element units per activation row
   const int rg = tid >= U16 ? 1 : 0;
   const int u = tid - rg * U16;           // the thread's unit
