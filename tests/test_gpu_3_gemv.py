@@ -191,6 +191,22 @@ def test_q8_rotation_blocks(M, block_len):
     assert_within_bound(_run(2, W, x, block_len, s), y_ref, b, TOL, f"q8 n={block_len} M={M}")
 
 
+@pytest.mark.parametrize("M,K,block_len", [(2, 5120, 2), (4, 5120, 16), (3, 1056, 16), (4, 1056, 0),
+                                           (2, 96, 8)])
+def test_q8_small_blocks_register_digits(M, K, block_len):
+    """Q8_0, two to four rows, rotation blocks of at most 16 (stages in
+    registers, digits made from registers, rows split over two thread
+    groups), with signs; K = 1056 puts both groups' units in one wave."""
+    N = 150
+    W = inputs.weights(730 + M, N, K)
+    x = inputs.activations(731 + M, M, K, offset=-0.4)
+    s = inputs.signs(732, K)
+    y_ref, b = _oracle_ref(2, W, x, block_len, s)
+    assert_within_bound(_run(2, W, x, block_len, s), y_ref, b, TOL, f"q8 K={K} n={block_len} M={M}")
+    assert_within_bound(_run(2, W, x, block_len, s, split_k=2), y_ref, b, TOL,
+                        f"q8 K={K} n={block_len} M={M} S=2")
+
+
 @pytest.mark.parametrize("M,block_len", [(1, 128), (3, 128), (1, 1024), (5, 1024)])
 def test_code_3_is_a_zero_weight(M, block_len):
     """Code 3 is not a PQ2_0 value (the format maps codes 0, 1 and 2); the
