@@ -177,15 +177,15 @@ struct GemvHead {
   int n;              // rows (fits 32 bits)
   int G;              // groups per row: 32 G code bytes a row, 256 ceil(G/8) scale bytes a tile
   int u_br;           // K slices of whole rotation blocks: u_base | u_rem << 16
-  int U;              // groups per rotation block
+  int unw;            // groups per rotation block | waves per workgroup << 8
 };
 #define KQ_HEAD_PARAMS                                                                        \
   const uint8_t *__restrict__ h_qs, const uint8_t *__restrict__ h_dpl,                       \
       const float *__restrict__ h_x, const int8_t *__restrict__ h_sg, int h_qb, int h_qr,    \
-      int h_n, int h_g, int h_ubr, int h_u
-#define KQ_HEAD_MAKE {h_qs, h_dpl, h_x, h_sg, h_qb, h_qr, h_n, h_g, h_ubr, h_u}
+      int h_n, int h_g, int h_ubr, int h_unw
+#define KQ_HEAD_MAKE {h_qs, h_dpl, h_x, h_sg, h_qb, h_qr, h_n, h_g, h_ubr, h_unw}
 #define KQ_HEAD_ARGS(h)                                                                       \
-  (h).qs, (h).dpl, (h).x, (h).signs, (h).q_base, (h).q_rem, (h).n, (h).G, (h).u_br, (h).U
+  (h).qs, (h).dpl, (h).x, (h).signs, (h).q_base, (h).q_rem, (h).n, (h).G, (h).u_br, (h).unw
 static_assert(sizeof(GemvHead) == 56, "the head is 14 preloaded dwords");
 
 __device__ __forceinline__ WgRows wg_rows_head(const GemvHead& h) {
@@ -440,32 +440,33 @@ __device__ __forceinline__ void reduce_round(const WgRows& a, const float* part,
 }
 
 // One activation row: each wave leaves one partial per output row (its four
-// lane blocks already added), [RBR][16 rows][NWP wave slots]; the NW of them
-// are added as a fixed tree, read as NWP / 4 16-byte words.
+// lane blocks already added), [RBR][16 rows][NWP wave slots]; the slots of
+// waves past NW hold zeros (written in the prologue), and the NWP slots are
+// added as a fixed tree, read as NWP / 4 16-byte words.
 template <int NWP>
-__device__ __forceinline__ void reduce_round_one(const WgRows& a, const float* part, int NW, int RBR,
+__device__ __forceinline__ float sum_slots(const float* pr) {
+  const float4* p = reinterpret_cast<const float4*>(pr);
+  float v[NWP];
+#pragma unroll
+  for (int q = 0; q < NWP / 4; ++q) {
+    const float4 f = p[q];
+    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+  }
+#pragma unroll
+  for (int h = 1; h < NWP; h *= 2)
+#pragma unroll
+    for (int w = 0; w + h < NWP; w += 2 * h) v[w] += v[w + h];
+  return v[0];
+}
+template <int NWP>
+__device__ __forceinline__ void reduce_round_one(const WgRows& a, const float* part, int RBR,
                                                  int rb0, int nrb, int round, int s) {
   const float* pr = part + (round & 1) * RBR * kRB * NWP;
   for (int it = threadIdx.x; it < RBR * kRB; it += blockDim.x) {
     const int jr = it / kRB, r = it % kRB;
     const int j = round * RBR + jr;
     const int row = (rb0 + j) * kRB + r;
-    if (j < nrb && row >= a.r0 && row < a.r1) {
-      const float4* p = reinterpret_cast<const float4*>(pr + it * NWP);
-      float v[NWP];
-#pragma unroll
-      for (int q = 0; q < NWP / 4; ++q) {
-        const float4 f = p[q];
-        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-      }
-#pragma unroll
-      for (int w = 0; w < NWP; ++w) v[w] = w < NW ? v[w] : 0.f;
-#pragma unroll
-      for (int h = 1; h < NWP; h *= 2)
-#pragma unroll
-        for (int w = 0; w + h < NWP; w += 2 * h) v[w] += v[w + h];
-      a.out[(int64_t)s * a.N + row] = v[0];
-    }
+    if (j < nrb && row >= a.r0 && row < a.r1) a.out[(int64_t)s * a.N + row] = sum_slots<NWP>(pr + it * NWP);
   }
 }
 
@@ -652,14 +653,18 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(KQ_HEA
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int NW = blockDim.x >> 6;
+  // waves per workgroup from the preloaded head (blockDim comes from a
+  // scalar load of the dispatch's implicit arguments, and its wait landed
+  // before the first weight loads)
+  const int NW = h.unw >> 8;
   const int r16 = lane & 15, kb = lane >> 4;
 
   int g0, g1;
   {
     const int ub = h.u_br & 0xFFFF, ur = h.u_br >> 16;
-    g0 = part_start(blockIdx.y, ub, ur) * h.U;
-    g1 = part_start(blockIdx.y + 1, ub, ur) * h.U;
+    const int U = h.unw & 0xFF;
+    g0 = part_start(blockIdx.y, ub, ur) * U;
+    g1 = part_start(blockIdx.y + 1, ub, ur) * U;
   }
   const uint32_t row_bytes = 32u * (uint32_t)h.G, d_tile_bytes = 256u * (uint32_t)((h.G + 7) >> 3);
   const int gw = g0 + wave * GS;                // first group of this wave
@@ -863,6 +868,16 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(KQ_HEA
   // only the compiler must not move the reads above the writes.
   uint8_t* zeros = lds + pq2_lds_zero_offset(M, NW, GS);
   if (lane < 2) *reinterpret_cast<uint4*>(zeros + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+  // the output's address and row count in scalar registers now (left to the
+  // compiler, their load from the argument block came after the final
+  // barrier, on the critical path)
+  asm volatile("" ::"s"(wr.out), "s"(wr.N));
+  if constexpr (ONE) {
+    // zeros in the partial slots of waves past NW: the sums need no mask
+    if (wave == 0)
+      for (int c = lane; c < 2 * RBR * kRB; c += 64)
+        for (int w = NW; w < NWP; ++w) part[c * NWP + w] = 0.f;
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -963,7 +978,7 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(KQ_HEA
     }
   };
   auto reduce = [&](int round) {
-    if constexpr (ONE) reduce_round_one<NWP>(wr, part, NW, RBR, rb0, nrb, round, blockIdx.y);
+    if constexpr (ONE) reduce_round_one<NWP>(wr, part, RBR, rb0, nrb, round, blockIdx.y);
     else reduce_round(wr, part, NW, RBR, M, KS, rb0, nrb, round, blockIdx.y);
   };
 
@@ -972,8 +987,20 @@ __global__ __launch_bounds__(Pq2Cfg<EPL>::MAXW * 64) void gemv_pq2_kernel(KQ_HEA
 #pragma unroll
     for (int i = 0; i < D; ++i)
       if (i < nrb) compute(wb[i], i);
-    __syncthreads();
-    reduce(0);
+    if constexpr (ONE) {
+      // the final sums' operands and destinations, ready before the barrier
+      // (at most D row blocks: threads [0, 16 D) hold one output each)
+      const int jr = threadIdx.x / kRB;
+      const int row = (rb0 + jr) * kRB + (int)(threadIdx.x % kRB);
+      const bool ok = jr < nrb && row >= wr.r0 && row < wr.r1;
+      float* dst = wr.out + (int64_t)blockIdx.y * wr.N + row;
+      const float* src = part + threadIdx.x * NWP;
+      __syncthreads();
+      if (ok) *dst = sum_slots<NWP>(src);
+    } else {
+      __syncthreads();
+      reduce(0);
+    }
     return;
   }
   for (int j0 = 0; j0 < nrb; j0 += D) {
@@ -1921,7 +1948,7 @@ static GemvHead head_of(const GemvArgs& a) {
   h.n = (int)a.N;
   h.G = a.G;
   h.u_br = a.u_base | a.u_rem << 16;
-  h.U = a.U;
+  h.unw = a.U;  // | waves << 8, set at launch
   return h;
 }
 
@@ -1931,7 +1958,8 @@ static int launch_kernel_head(Kernel k, const GemvArgs& a, const GemvPlan& p, hi
       hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
           hipSuccess)
     return -1;
-  const GemvHead h = head_of(a);
+  GemvHead h = head_of(a);
+  h.unw |= p.nw << 8;
   hipLaunchKernelGGL(k, dim3(p.grid_x, p.split), dim3(p.nw * 64), p.lds_bytes, st, KQ_HEAD_ARGS(h), a);
   return 0;
 }
