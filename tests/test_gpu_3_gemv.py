@@ -137,6 +137,20 @@ def test_block_lengths(block_len):
     assert_within_bound(_run(1, W, x, block_len, s), y_ref, b, TOL, f"n={block_len}")
 
 
+@pytest.mark.parametrize("N,K,split_k", [(1, 128, 1), (17, 640, 1), (17, 640, 2), (33, 2048, 1),
+                                         (33, 2048, 2), (300, 5120, 1), (300, 5120, 2),
+                                         (4097, 1152, 1), (4097, 1152, 2)])
+def test_pq2_one_row_shapes(N, K, split_k):
+    """PQ2_0, one activation row, at wave counts 1 to 10 and ragged row
+    counts: the instance whose workgroups own at most three row blocks (its
+    final sum reads zero-filled slots of absent waves) and the looping one."""
+    W = inputs.weights(760 + N, N, K)
+    x = inputs.activations(761 + N, 1, K, offset=0.2)
+    y_ref, b = _oracle_ref(1, W, x, 128)
+    assert_within_bound(_run(1, W, x, 128, split_k=split_k), y_ref, b, TOL,
+                        f"N={N} K={K} S={split_k}")
+
+
 @pytest.mark.parametrize("M", [2, 4, 5, 8])
 @pytest.mark.parametrize("block_len", [512, 1024])
 def test_block_lengths_many_rows(M, block_len):
